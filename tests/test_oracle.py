@@ -1,0 +1,352 @@
+"""Pins for the CPU fp64 oracle, checked against things other than itself.
+
+Each test ties one part of the oracle to an independent source: hand-derived
+tree fixtures, a library routine (torch scaled_dot_product_attention in fp64)
+on special cases, exact brute force with math.fsum on tiny shapes, closed
+forms (q = 0, a single key, a dominant "needle" key), invariants (pool
+permutation, normalisation, partition-and-merge) and a statistical limit.
+A plausible slip anywhere in the oracle (dropped scale or rope columns, a
+wrong sign, an off-by-one in the mask, the table index skipped, V taken from
+the wrong columns) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_tree_verify_mla_amd import inputs
+from conftest import load_tree_fixtures
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+SM = inputs.SM_SCALE
+
+
+def _f64(bits):
+    return inputs.bf16_to_f32(bits).astype(np.float64)
+
+
+def _small(seed, H=2, T=4, L=8, num_slots=64, tree="random", table="scattered", B=1):
+    return inputs.make_workload("t", H, [T] * B, [L] * B, num_slots, seed=seed, table=table,
+                                tree=tree)
+
+
+# ----------------------------------------------------------------- tree mask
+@pytest.mark.parametrize("fx", load_tree_fixtures(), ids=lambda f: f[0])
+def test_tree_visibility_matches_hand_fixtures(fx):
+    name, parent, vis = fx
+    got = oracle.tree_visibility(parent)
+    T = len(parent)
+    for i in range(T):
+        assert set(np.flatnonzero(got[i]).tolist()) == vis[i], (name, i)
+
+
+@pytest.mark.parametrize("bad", [[0], [-1, 1], [-1, 0, 5], [-2]])
+def test_tree_visibility_rejects_bad_parent(bad):
+    with pytest.raises(oracle.OracleError):
+        oracle.tree_visibility(bad)
+
+
+# ----------------------------------------------------------------- library special cases
+def _sdpa_reference(wl, r=0):
+    """torch fp64 SDPA over the gathered keys with an explicit boolean mask."""
+    H = wl.num_heads
+    T = int(wl.num_tree[r])
+    L = int(wl.prefix_len[r])
+    t0 = int(wl.num_tree[:r].sum())
+    tab = wl.slot_table[wl.slot_indptr[r]:wl.slot_indptr[r] + L + T]
+    kv = torch.from_numpy(_f64(wl.kv_pool[tab]))                         # [n, 576]
+    q = torch.from_numpy(_f64(wl.q[t0:t0 + T])).permute(1, 0, 2)         # [H, T, 576]
+    vis = oracle.tree_visibility(wl.parent[t0:t0 + T])                   # pinned above
+    mask = torch.zeros(T, L + T, dtype=torch.bool)
+    mask[:, :L] = True
+    mask[:, L:] = torch.from_numpy(vis)
+    k = kv.unsqueeze(0).expand(H, -1, -1)
+    v = kv[:, :512].unsqueeze(0).expand(H, -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=SM)
+    s = SM * torch.matmul(q, kv.t())
+    s = s.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.permute(1, 0, 2).numpy(), lse.t().numpy()
+
+
+@pytest.mark.parametrize("L,T", [(0, 4), (5, 4), (37, 8), (300, 16)])
+def test_chain_tree_equals_causal_attention(L, T):
+    """A chain tree is causal attention with query i at position L + i."""
+    wl = inputs.make_workload("chain", 3, [T], [L], 512, seed=11 + L, tree="chain")
+    out, lse = oracle.verify_attn_workload(wl)
+    H = wl.num_heads
+    tab = wl.slot_table[:L + T]
+    kv = torch.from_numpy(_f64(wl.kv_pool[tab]))
+    q = torch.from_numpy(_f64(wl.q)).permute(1, 0, 2)
+    causal = torch.ones(T, L + T, dtype=torch.bool).tril(diagonal=L)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, kv.unsqueeze(0).expand(H, -1, -1), kv[:, :512].unsqueeze(0).expand(H, -1, -1),
+        attn_mask=causal, scale=SM).permute(1, 0, 2).numpy()
+    s = (SM * torch.matmul(q, kv.t())).masked_fill(~causal, float("-inf"))
+    ref_lse = torch.logsumexp(s, dim=-1).t().numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_single_node_is_plain_decode_attention():
+    """T = 1: one query over L + 1 keys with no mask at all."""
+    wl = inputs.make_workload("t1", 4, [1], [200], 512, seed=5)
+    out, lse = oracle.verify_attn_workload(wl)
+    kv = torch.from_numpy(_f64(wl.kv_pool[wl.slot_table]))
+    q = torch.from_numpy(_f64(wl.q[0]))                                  # [H, 576]
+    ref = torch.softmax(SM * q @ kv.t(), dim=-1) @ kv[:, :512]
+    ref_lse = torch.logsumexp(SM * q @ kv.t(), dim=-1)
+    np.testing.assert_allclose(out[0], ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], ref_lse.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed,T,L", [(1, 9, 40), (2, 16, 3), (3, 32, 100), (4, 64, 17)])
+def test_random_tree_equals_masked_sdpa(seed, T, L):
+    wl = inputs.make_workload("tree", 2, [T], [L], 1024, seed=seed)
+    out, lse = oracle.verify_attn_workload(wl)
+    ref, ref_lse = _sdpa_reference(wl)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_ragged_batch_each_request_matches_sdpa():
+    wl = inputs.make_workload("rag", 2, [3, 7, 1], [0, 33, 9], 512, seed=21, table="interleaved")
+    out, lse = oracle.verify_attn_workload(wl)
+    t0 = 0
+    for r in range(3):
+        T = int(wl.num_tree[r])
+        ref, ref_lse = _sdpa_reference(wl, r)
+        np.testing.assert_allclose(out[t0:t0 + T], ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[t0:t0 + T], ref_lse, rtol=0, atol=1e-12)
+        t0 += T
+
+
+# ----------------------------------------------------------------- brute force
+def _brute_force(wl):
+    """Per element, pure Python: walk the parents, sum with math.fsum."""
+    H = wl.num_heads
+    T = int(wl.num_tree[0])
+    L = int(wl.prefix_len[0])
+    par = [int(p) for p in wl.parent]
+    kvf = _f64(wl.kv_pool)
+    qf = _f64(wl.q)
+    out = np.zeros((T, H, 512))
+    lse = np.zeros((T, H))
+    for i in range(T):
+        seen = set()
+        a = i
+        while a != -1:
+            seen.add(a)
+            a = par[a]
+        keys = list(range(L)) + [L + j for j in range(T) if j in seen]
+        for h in range(H):
+            s = []
+            for k in keys:
+                row = kvf[wl.slot_table[k]]
+                s.append(SM * math.fsum(float(qf[i, h, d]) * float(row[d]) for d in range(576)))
+            z = math.fsum(math.exp(x) for x in s)
+            lse[i, h] = math.log(z)
+            for c in range(512):
+                out[i, h, c] = math.fsum(math.exp(x) / z * float(kvf[wl.slot_table[k], c])
+                                         for x, k in zip(s, keys))
+    return out, lse
+
+
+@pytest.mark.parametrize("seed,H,T,L", [(31, 1, 1, 0), (32, 2, 4, 8), (33, 2, 3, 5), (34, 1, 4, 1)])
+def test_brute_force_tiny(seed, H, T, L):
+    wl = inputs.make_workload("bf", H, [T], [L], 32, seed=seed)
+    out, lse = oracle.verify_attn_workload(wl)
+    ref, ref_lse = _brute_force(wl)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- invariants
+def test_pool_permutation_invariance():
+    """Moving rows around the pool and remapping the table changes nothing."""
+    wl = inputs.make_workload("perm", 2, [8], [50], 256, seed=41)
+    out, lse = oracle.verify_attn_workload(wl)
+    rng = np.random.default_rng(7)
+    pi = rng.permutation(wl.num_slots)           # new position of old slot s is pi[s]
+    pool2 = np.empty_like(wl.kv_pool)
+    pool2[pi] = wl.kv_pool
+    out2, lse2 = oracle.verify_attn(wl.num_heads, wl.num_tree, wl.prefix_len, wl.q, pool2,
+                                    pi[wl.slot_table].astype(np.int32), wl.slot_indptr,
+                                    wl.parent, wl.sm_scale)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+    # and the pool content matters: the identity table on the moved pool differs
+    out3, _ = oracle.verify_attn(wl.num_heads, wl.num_tree, wl.prefix_len, wl.q, pool2,
+                                 wl.slot_table, wl.slot_indptr, wl.parent, wl.sm_scale)
+    assert np.abs(out3 - out).max() > 1e-3
+
+
+def test_probabilities_normalised_and_masked_exactly_zero():
+    wl = inputs.make_workload("probs", 2, [12], [20], 128, seed=43)
+    out, lse, p = oracle.verify_attn_workload(wl, return_probs=True)
+    L, T, H = 20, 12, 2
+    vis = oracle.tree_visibility(wl.parent)
+    p = p.reshape(T, H, L + T)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-14)
+    for i in range(T):
+        hidden = [L + j for j in range(T) if not vis[i, j]]
+        shown = [L + j for j in range(T) if vis[i, j]]
+        assert (p[i][:, hidden] == 0.0).all()
+        assert (p[i][:, shown] > 0.0).all()
+        assert (p[i][:, :L] > 0.0).all()
+    # o is the p-weighted average of the value columns
+    kvf = _f64(wl.kv_pool[wl.slot_table])
+    np.testing.assert_allclose(out, np.einsum("thk,kc->thc", p, kvf[:, :512]), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cut_seed", [0, 1, 2])
+def test_partition_and_merge_equals_whole(cut_seed):
+    """Attend over arbitrary disjoint parts, merge by LSE: equals the whole."""
+    wl = inputs.make_workload("merge", 1, [1], [300], 1024, seed=47)
+    qf = _f64(wl.q[0, 0])
+    slots = wl.slot_table
+    o_all, lse_all, _ = oracle.attend(qf, wl.kv_pool, slots, SM)
+    rng = np.random.default_rng(cut_seed)
+    perm = rng.permutation(len(slots))
+    cuts = np.sort(rng.choice(np.arange(1, len(slots)), size=6, replace=False))
+    parts = np.split(perm, cuts) + [np.zeros(0, dtype=np.int64)]          # plus an empty part
+    os_, ls_ = [], []
+    for part in parts:
+        o, l, _ = oracle.attend(qf, wl.kv_pool, slots[part], SM)
+        os_.append(o)
+        ls_.append(l)
+    o, l = oracle.lse_merge(np.stack(os_), np.array(ls_))
+    np.testing.assert_allclose(o, o_all, rtol=0, atol=1e-12)
+    assert abs(l - lse_all) < 1e-12
+
+
+def test_merge_of_single_part_is_identity_and_empty_is_neutral():
+    o = np.linspace(-1, 1, 512)
+    m, l = oracle.lse_merge(o[None], np.array([3.25]))
+    np.testing.assert_array_equal(m, o)
+    assert l == 3.25
+    m, l = oracle.lse_merge(np.stack([o, np.full(512, 7.0)]), np.array([3.25, -np.inf]))
+    np.testing.assert_array_equal(m, o)
+    assert l == 3.25
+
+
+# ----------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257])
+def test_zero_query_gives_uniform_weights(L):
+    """q = 0: every visible key gets 1/n_i; lse = ln n_i; o = mean of visible V."""
+    T, H = 6, 2
+    wl = inputs.make_workload("q0", H, [T], [L], 1024, seed=53 + L,
+                              q_override=np.zeros((T, H, 576), dtype=np.uint16))
+    out, lse = oracle.verify_attn_workload(wl)
+    vis = oracle.tree_visibility(wl.parent)
+    kvf = _f64(wl.kv_pool[wl.slot_table])[:, :512]
+    for i in range(T):
+        keys = list(range(L)) + [L + j for j in range(T) if vis[i, j]]
+        n_i = len(keys)
+        assert np.all(np.abs(lse[i] - math.log(n_i)) < 1e-12)
+        np.testing.assert_allclose(out[i], np.broadcast_to(kvf[keys].mean(0), (H, 512)),
+                                   rtol=0, atol=1e-12)
+
+
+def test_single_key():
+    """L = 0, T = 1: o equals the node's own value row, lse its own score."""
+    wl = inputs.make_workload("one", 3, [1], [0], 16, seed=59)
+    out, lse = oracle.verify_attn_workload(wl)
+    row = _f64(wl.kv_pool[wl.slot_table[0]])
+    for h in range(3):
+        np.testing.assert_array_equal(out[0, h], row[:512])
+        s = SM * math.fsum(float(a) * float(b) for a, b in zip(_f64(wl.q[0, h]), row))
+        assert abs(lse[0, h] - s) < 1e-12
+
+
+def _needle_workload(L, T, key, seed, margin=60.0):
+    """One query row per node; the pool row at logical key `key` is set to a
+    scaled copy of q so its score beats every other key by > margin."""
+    H = 1
+    wl = inputs.make_workload("needle", H, [T], [L], 4 * (L + T) + 64, seed=seed, tree="random")
+    # needle score sm_scale*0.5*4*576 ~ 83; other scores have std ~ 0.87
+    q = inputs.bf16_bits(np.full((T, H, 576), 0.5, dtype=np.float32))
+    wl.q = q
+    slot = wl.slot_table[key]
+    big = inputs.bf16_bits(np.full(576, 4.0, dtype=np.float32))
+    wl.kv_pool = wl.kv_pool.copy()
+    wl.kv_pool[slot] = big
+    return wl
+
+
+@pytest.mark.parametrize("L,key", [(100, 0), (100, 31), (100, 32), (100, 99), (64, 63)])
+def test_needle_in_prefix_is_seen_by_every_node(L, key):
+    T = 8
+    wl = _needle_workload(L, T, key, seed=61 + key)
+    out, lse = oracle.verify_attn_workload(wl)
+    row = _f64(wl.kv_pool[wl.slot_table[key]])
+    s = SM * 0.5 * 4.0 * 576
+    for i in range(T):
+        np.testing.assert_allclose(out[i, 0], row[:512], rtol=0, atol=1e-12)
+        assert abs(lse[i, 0] - s) < 1e-9
+
+
+def test_needle_on_draft_node_seen_only_by_descendants():
+    L, T = 40, 12
+    wl = inputs.make_workload("nd", 1, [T], [L], 512, seed=67)
+    vis = oracle.tree_visibility(wl.parent)
+    for j in range(T):
+        w2 = _needle_workload(L, T, L + j, seed=67)
+        w2.parent = wl.parent
+        out, lse = oracle.verify_attn_workload(w2)
+        row = _f64(w2.kv_pool[w2.slot_table[L + j]])
+        for i in range(T):
+            near = np.abs(out[i, 0] - row[:512]).max() < 1e-12
+            assert near == bool(vis[i, j]), (i, j)
+
+
+# ----------------------------------------------------------------- statistical limit
+def test_large_prefix_statistical_limit():
+    """N(0,1) keys: exponential tilting gives o -> sm_scale*q[:512] and
+    lse -> ln n + sm_scale^2 |q|^2 / 2 (sanity of scale and columns)."""
+    L = 65536
+    wl = inputs.make_workload("big", 1, [2], [L], L + 64, seed=71, table="contiguous")
+    out, lse = oracle.verify_attn_workload(wl)
+    for i in range(2):
+        q = _f64(wl.q[i, 0])
+        vis_n = L + (1 if wl.parent[i] == -1 else 2)
+        pred_lse = math.log(vis_n) + SM * SM * float(q @ q) / 2
+        assert abs(lse[i, 0] - pred_lse) < 0.15
+        corr = np.corrcoef(out[i, 0], SM * q[:512])[0, 1]
+        assert corr > 0.9
+
+
+# ----------------------------------------------------------------- errors
+def test_bad_slot_and_short_table_are_errors():
+    wl = _small(73)
+    bad = wl.slot_table.copy()
+    bad[3] = wl.num_slots
+    with pytest.raises(oracle.OracleError):
+        oracle.verify_attn(wl.num_heads, wl.num_tree, wl.prefix_len, wl.q, wl.kv_pool, bad,
+                           wl.slot_indptr, wl.parent, SM)
+    short = wl.slot_indptr.copy()
+    short[-1] -= 1
+    with pytest.raises(oracle.OracleError):
+        oracle.verify_attn(wl.num_heads, wl.num_tree, wl.prefix_len, wl.q, wl.kv_pool,
+                           wl.slot_table, short, wl.parent, SM)
+
+
+def test_row_selection_computes_only_selected_rows():
+    wl = _small(79, H=2, T=4, L=8)
+    full, full_lse = oracle.verify_attn_workload(wl)
+    part, part_lse = oracle.verify_attn_workload(wl, rows=[1, 6])
+    flat = part.reshape(-1, 512)
+    np.testing.assert_array_equal(flat[[1, 6]], full.reshape(-1, 512)[[1, 6]])
+    assert np.isnan(flat[0]).all()
+    np.testing.assert_array_equal(part_lse.reshape(-1)[[1, 6]], full_lse.reshape(-1)[[1, 6]])
+
+
+def test_threads_do_not_change_results():
+    wl = _small(83, H=2, T=8, L=100, num_slots=256)
+    a, la = oracle.verify_attn_workload(wl, num_threads=1)
+    b, lb = oracle.verify_attn_workload(wl, num_threads=4)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
