@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of one tree-verify MLA attention step on one MI355X.
+
+A step is one verify call (verify_attn_run + verify_attn_reduce) over the
+long-prefix tensor-parallel-rank workload: 1 request, H=8 heads, T=16 draft
+nodes in a random tree, prefix L=65536, a 262144-slot bf16 pool whose slot
+table is half contiguous runs (length 1..64) and half scattered slots.
+
+Timing: the steps are captured in a HIP graph and replayed on the current
+stream between two HIP events.  Each step reads a different copy of the pool
+(8 copies, 2.4 GB), so consecutive calls do not hit the 256 MB Infinity
+Cache with the previous call's 75.5 MB of KV rows; a warm variant (one pool)
+is reported beside it.  The partial-pass kernel is also timed alone (a graph
+of run-only launches) for the roofline line.
+
+Metric: effective KV GB/s = (L + T) * 1152 bytes (each 576-wide bf16 latent
+row read once per call, shared by every head) / time per call.
+
+CPU baseline: the fp64 oracle (tests' reference) on the same workload, on
+the host cores, full verify calls repeated for a bounded ~10-30 s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+WORKLOAD = 3                   # 1 request, H=8, T=16, L=65536
+N_POOLS = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--pools", type=int, default=N_POOLS)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--eager", action="store_true", help="launch without graph capture")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU verify path only; this build runs on one GPU "
+              "(use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_tree_verify_mla_amd as va
+    from speculative_tree_verify_mla_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = inputs.make_config(WORKLOAD)
+    print(f"# workload {wl.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q = to_dev(wl.q.view(np.int16)).view(torch.bfloat16)
+    pool0 = to_dev(wl.kv_pool.view(np.int16)).view(torch.bfloat16)
+    pools = [pool0] + [pool0.clone() for _ in range(max(0, args.pools - 1))]
+    table = to_dev(wl.slot_table)
+    indptr = to_dev(wl.slot_indptr)
+    prefix = to_dev(wl.prefix_len)
+    parent = to_dev(wl.parent)
+    H = wl.num_heads
+    T = int(wl.num_tree.sum())
+
+    plan = va.verify_attn_plan(H, wl.prefix_len, wl.num_tree)
+    ws = va.workspace_for(plan, dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+
+    def step(i, reduce=True, pool_set=None):
+        ps = pools if pool_set is None else pool_set
+        va.verify_attn_run(plan, q, ps[i % len(ps)], table, indptr, prefix, parent, wl.sm_scale,
+                           ws, stream)
+        if reduce:
+            va.verify_attn_reduce(plan, ws, out, lse, stream)
+
+    def capture(n, reduce=True, pool_set=None):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    step(i, reduce, pool_set)
+        return g
+
+    def timed(n, reduce=True, pool_set=None):
+        """Run n steps between two syncs; return (ms from HIP events recorded on
+        `stream` around the steps, host wall seconds between the syncs)."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        g = None if args.eager else capture(n, reduce, pool_set)
+        torch.cuda.synchronize()
+        w0 = time.time()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            if g is None:
+                for i in range(n):
+                    step(i, reduce, pool_set)
+            else:
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.time() - w0
+
+    # correctness of this exact launch configuration against the eager path
+    step(0)
+    torch.cuda.synchronize()
+    status = va.verify_attn_read_status(plan, ws, stream)
+    if status != 0:
+        raise RuntimeError(f"device status {status}")
+    ref_out = out.clone()
+
+    K, W = args.steps, args.warmup
+    if W > 0:
+        timed(W)
+    ms, t_wall = timed(K)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "graph output differs"
+    ms_per_step = ms / K
+    ms_partial = timed(K, reduce=False)[0] / K
+    ms_warm = timed(K, pool_set=[pools[0]])[0] / K
+    ms_partial_warm = timed(K, reduce=False, pool_set=[pools[0]])[0] / K
+    print(f"# timed {K} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    kv_bytes = wl.kv_bytes()
+    n_keys = wl.num_keys
+    rows = wl.total_rows
+    flops = 2.0 * rows * n_keys * (576 + 512)
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    gbs_partial = kv_bytes / (ms_partial * 1e-3) / 1e9
+
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# calibration copy of {nbytes} bytes x3 done", file=sys.stderr, flush=True)
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+        reps = 0
+        t_cpu = 0.0
+        ref = None
+        while reps == 0 or (t_cpu < args.cpu_seconds and reps < 20):
+            c0 = time.time()
+            ref, ref_lse = oracle.verify_attn_workload(wl, num_threads=threads)
+            t_cpu += time.time() - c0
+            reps += 1
+        per_call = t_cpu / reps
+        cpu = {"value": round(kv_bytes / per_call / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{reps} full verify call(s) of the bench workload "
+                         f"({rows} rows x {n_keys} keys, fp64), {per_call * 1e3:.0f} ms/call"}
+        got = ref_out.float().cpu().numpy().astype(np.float64)
+        parity = {"max_abs_out": float(np.abs(got - ref).max()),
+                  "max_abs_lse": float(np.abs(lse.cpu().numpy() - ref_lse).max())}
+
+    result = {
+        "metric": "effective KV GB/s (% HBM peak) + us/verify call @65k prefix, H=8, T=16",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "requests": 1, "num_heads": H, "num_tree": T,
+            "prefix_len": int(wl.prefix_len[0]), "num_slots": wl.num_slots,
+            "slot_table": "50% runs of 1-64 consecutive slots, 50% scattered",
+            "tree": "random, depth<=6", "pools_rotated": len(pools),
+            "timing": "eager" if args.eager else "hip graph replay",
+        },
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "mfma_util_pct": round(100.0 * flops / (ms_per_step * 1e-3) / 1e12
+                               / BF16_DENSE_PEAK_TFLOPS, 2),
+        "warm_us_per_call": round(ms_warm * 1e3, 3),
+        "warm_value": round(kv_bytes / (ms_warm * 1e-3) / 1e9, 2),
+        "nsplit": plan.splits(),
+        "work_items": int(plan.total_work),
+        "kv_bytes_per_call": kv_bytes,
+        "roofline": {
+            "kernel": "va_partial_kernel",
+            "bound": "hbm",
+            "achieved": round(gbs_partial, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs_partial / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_us": round(ms_partial * 1e3, 3),
+            "warm_avg_us": round(ms_partial_warm * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

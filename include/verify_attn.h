@@ -1,0 +1,223 @@
+/*
+ * verify_attn.h - C ABI of the MI355X (gfx950) tree-verify MLA attention library.
+ *
+ * The operation: for every draft-tree node i of a request and every head h,
+ * weight-absorbed MLA attention of the 576-wide query q[i,h] (512 latent +
+ * 64 rope columns) over the request's latent KV rows, which live one token
+ * per slot (page_size 1) in a shared pool and are reached through a
+ * per-token slot table.  Node i sees the whole prefix (no mask), itself and
+ * its ancestors in the draft tree; it never sees siblings or descendants.
+ *   score_k = sm_scale * <q[i,h], K_k>        (K_k = all 576 columns of row k)
+ *   lse     = ln sum_k exp(score_k)           (over the visible keys)
+ *   out     = sum_k exp(score_k - lse) * V_k  (V_k = first 512 columns of row k)
+ *
+ * Sources: "The Execution Phase: From Plan to 3-6x Decode Speedup on
+ * Blackwell Consumer GPUs" (section "The Transition: From Planning to
+ * Execution": a C API called through ctypes, around MLA-absorb attention
+ * with a custom tree mask; section "Making the Kernel CUDA Graph
+ * Capture-Safe": static buffers, no host sync, no device allocation, a
+ * caller-owned workspace, a split count fixed ahead of capture); "The
+ * Verify Kernel Breakthrough" (section "The Message in Context": split-KV
+ * flash-decode with a partial pass and a reduce); "The Architecture
+ * Detective" (section "The Split Verify Design": dense prefix, masked tree
+ * block, log-sum-exp merge).
+ *
+ * Three calls make one verify step:
+ *   verify_attn_plan   host only; sizes the split-KV work and the workspace.
+ *   verify_attn_run    partial pass: every (request, row group, KV split)
+ *                      work item writes a partial (o, lse) into the workspace.
+ *   verify_attn_reduce log-sum-exp merge of the partials into out and lse.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named h_* are host pointers; every other data pointer is a
+ *     device pointer.  bf16 tensors are passed as uint16_t bit patterns.
+ *   - The caller owns all memory.  The library never allocates or frees
+ *     device memory and never synchronises; run and reduce only enqueue
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream), so the
+ *     pair can be captured into a HIP graph.  Call plan outside capture.
+ *   - Return value: VA_OK (0) or a negative VA_ERR_* code.  No exception
+ *     crosses the ABI.  Argument errors are found on the host before any
+ *     launch; faulty device-resident data (a slot outside the pool, a bad
+ *     parent, a prefix length above the planned bound, a short slot table)
+ *     is never dereferenced: the affected rows come out as NaN and the
+ *     workspace records the error (verify_attn_read_status).
+ *   - One workspace serves one run/reduce pair at a time; concurrent steps
+ *     need separate workspaces.
+ */
+#ifndef VERIFY_ATTN_H
+#define VERIFY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VA_D_QK 576         /* query / key width: 512 latent + 64 rope */
+#define VA_D_V 512          /* value width: the latent columns */
+#define VA_MAX_TREE 64      /* draft nodes per request (one 64-bit ancestor mask) */
+#define VA_MAX_REQUESTS 64  /* requests per plan */
+#define VA_MAX_SPLITS 256   /* KV splits per request */
+#define VA_MAX_HEADS 1024
+
+/* Return codes. */
+#define VA_OK 0
+#define VA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define VA_ERR_SHAPE (-2)       /* count out of range (B, H, T, L, stride, num_slots) */
+#define VA_ERR_ALIGN (-3)       /* q/kv/out not 16-byte aligned, or stride not a multiple of 8 */
+#define VA_ERR_WORKSPACE (-4)   /* workspace NULL, misaligned or smaller than planned */
+#define VA_ERR_PLAN (-5)        /* plan not produced by verify_attn_plan of this version */
+#define VA_ERR_HIP (-6)         /* a HIP call or kernel launch failed */
+#define VA_ERR_TREE (-7)        /* parent[] is not a topological forest */
+#define VA_ERR_DEVICE_DATA (-8) /* device data failed the in-kernel checks (status word) */
+
+/* Bits of the device status word (verify_attn_read_status). */
+#define VA_STATUS_BAD_PREFIX 1u  /* prefix_len[r] < 0 or above the planned bound */
+#define VA_STATUS_SHORT_TABLE 2u /* slot_indptr gives fewer than L + T entries or leaves the table */
+#define VA_STATUS_BAD_SLOT 4u    /* a slot outside [0, num_slots) */
+#define VA_STATUS_BAD_PARENT 8u  /* parent[i] outside [-1, i-1] */
+
+typedef void* va_stream_t; /* a hipStream_t */
+
+/*
+ * Launch plan: a plain struct the caller allocates (stack, static or heap);
+ * it owns no resources and is never freed.  Its content is filled by
+ * verify_attn_plan and is read-only for the caller.
+ */
+typedef struct va_plan {
+  uint32_t magic;            /* VA_PLAN_MAGIC when valid */
+  uint32_t version;          /* VA_PLAN_VERSION */
+  int32_t num_requests;      /* B */
+  int32_t num_heads;         /* H */
+  int32_t rows_per_group;    /* query rows (node, head) one work item holds */
+  int32_t tile_keys;         /* keys per KV tile; split lengths are multiples of it */
+  int32_t total_work;        /* work items of the partial pass (its grid) */
+  int32_t total_tree;        /* sum of T_r */
+  int32_t total_rows;        /* sum of T_r * H */
+  int32_t num_cus;           /* compute units the plan was sized for */
+  int64_t workspace_bytes;   /* bytes verify_attn_run needs */
+  int64_t lse_offset;        /* byte offset of the partial-lse region */
+  int64_t status_offset;     /* byte offset of the per-work-item status words */
+  int32_t num_tree[VA_MAX_REQUESTS];        /* T_r */
+  int32_t max_prefix[VA_MAX_REQUESTS];      /* planned upper bound of L_r */
+  int32_t nsplit[VA_MAX_REQUESTS];          /* KV splits of request r */
+  int32_t num_groups[VA_MAX_REQUESTS];      /* row groups of request r */
+  int32_t tree_begin[VA_MAX_REQUESTS + 1];  /* prefix sums of T_r */
+  int32_t work_begin[VA_MAX_REQUESTS + 1];  /* prefix sums of groups * splits */
+} va_plan;
+
+#define VA_PLAN_MAGIC 0x56415054u /* "VAPT" */
+#define VA_PLAN_VERSION 1u
+
+/*
+ * verify_attn_plan - size the split-KV schedule and the workspace (host only).
+ *
+ * num_requests   B, 1..VA_MAX_REQUESTS.
+ * num_heads      H, 1..VA_MAX_HEADS.
+ * h_prefix_len   [B] host: prefix length L_r of each request, >= 0.  For a
+ *                captured graph pass an upper bound; the device value given
+ *                to run may be anything from 0 up to it.
+ * h_num_tree     [B] host: draft nodes T_r, 1..VA_MAX_TREE.  Fixed by the plan.
+ * num_cus        compute units to size the schedule for; 0 = ask the current
+ *                HIP device (the only device call this function makes).
+ * plan           out: caller-allocated plan.
+ * workspace_bytes out (may be NULL): bytes of device workspace run needs
+ *                (also plan->workspace_bytes).
+ *
+ * The number of KV splits per request (the grid dimension of the partial
+ * pass; "The Verify Kernel Breakthrough", section "The Message in Context",
+ * raised it from 16 to 64 for occupancy) is chosen from the compute-unit
+ * count, the rows T_r*H and the key counts so that every work item gets a
+ * similar number of keys.  The environment variable VA_NSPLIT, read here
+ * only, forces one split count for every request (for tuning sweeps).
+ * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_HIP (device query failed).
+ */
+int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
+                     const int32_t* h_num_tree, int32_t num_cus, va_plan* plan,
+                     size_t* workspace_bytes);
+
+/*
+ * verify_attn_run - partial pass (enqueue only).
+ *
+ * plan           from verify_attn_plan (host pointer; read during the call only).
+ * q              [sum T_r, H, 576] bf16, rows ordered (request, node, head);
+ *                16-byte aligned.
+ * kv_pool        [num_slots, kv_row_stride] bf16; columns 0..511 latent,
+ *                512..575 rope; 16-byte aligned.
+ * num_slots      rows in the pool (>= 1); slots are checked against it.
+ * kv_row_stride  elements between pool rows, >= 576 and a multiple of 8.
+ * slot_table     int32 [slot_table_len], per request L_r prefix slots in
+ *                logical order then T_r draft slots in node order, requests
+ *                concatenated.
+ * slot_table_len entries in slot_table; every table read is checked against it.
+ * slot_indptr    [B+1] int32: request r uses slot_table[slot_indptr[r] ...
+ *                slot_indptr[r+1]), which must hold at least L_r + T_r entries.
+ * prefix_len     [B] int32 device: actual L_r, 0..planned bound.
+ * parent         [sum T_r] int32, request-local: parent[i] in [-1, i-1]
+ *                (-1: the node hangs directly off the prefix).
+ * sm_scale       softmax scale applied to <q, k> (the workloads use 1/sqrt(192)).
+ * workspace      device scratch of at least plan->workspace_bytes, 256-byte
+ *                aligned; needs no initialisation.
+ * stream         hipStream_t to enqueue on.
+ * Errors: VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_SHAPE, VA_ERR_ALIGN,
+ *         VA_ERR_WORKSPACE, VA_ERR_HIP.
+ */
+int verify_attn_run(const va_plan* plan, const uint16_t* q, const uint16_t* kv_pool,
+                    int64_t num_slots, int32_t kv_row_stride, const int32_t* slot_table,
+                    int32_t slot_table_len, const int32_t* slot_indptr, const int32_t* prefix_len,
+                    const int32_t* parent, float sm_scale, void* workspace,
+                    size_t workspace_bytes, va_stream_t stream);
+
+/*
+ * verify_attn_reduce - merge the partials by log-sum-exp (enqueue only).
+ *
+ * workspace      the workspace the preceding verify_attn_run wrote.
+ * out            [sum T_r, H, 512] bf16 (round to nearest even); 16-byte aligned.
+ * lse            [sum T_r, H] fp32: natural log of the partition sum of the
+ *                scaled scores over the row's visible keys.
+ * Rows whose request failed the device checks get NaN in out and lse.
+ * Errors: VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_ALIGN, VA_ERR_HIP.
+ */
+int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out, float* lse,
+                       va_stream_t stream);
+
+/*
+ * verify_attn_read_status - OR of the device status words the last run wrote
+ * (VA_STATUS_* bits) into *h_status.  Diagnostic: it copies to the host and
+ * synchronises `stream`, so it must not be called under graph capture.
+ * Errors: VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_HIP.
+ */
+int verify_attn_read_status(const va_plan* plan, const void* workspace, va_stream_t stream,
+                            uint32_t* h_status);
+
+/*
+ * verify_attn_check_tree - host validator for one request's parent array:
+ * VA_OK when every parent[i] is in [-1, i-1] and 1 <= T <= VA_MAX_TREE,
+ * else VA_ERR_TREE (VA_ERR_NULL for a NULL pointer).
+ */
+int verify_attn_check_tree(const int32_t* h_parent, int32_t T);
+
+/*
+ * verify_attn_gather_rows - diagnostic copy of pool rows through the same
+ * 16-byte gather path the partial pass uses: dst[k, 0:576] =
+ * kv_pool[slot_table[k], 0:576] for k < n.  dst is [n, 576] bf16, 16-byte
+ * aligned.  Slots outside [0, num_slots) yield rows of NaN.  Enqueue only.
+ * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_ALIGN, VA_ERR_HIP.
+ */
+int verify_attn_gather_rows(const uint16_t* kv_pool, int64_t num_slots, int32_t kv_row_stride,
+                            const int32_t* slot_table, int32_t n, uint16_t* dst,
+                            va_stream_t stream);
+
+/* Static text for a return code. */
+const char* verify_attn_error_string(int code);
+
+/* sizeof(va_plan) as compiled into the library, for bindings to check
+ * their mirror of the struct. */
+size_t verify_attn_plan_struct_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_ATTN_H */

@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the plan (pure host code) sizes work and workspace as
+documented, and argument errors are caught on the host before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import speculative_tree_verify_mla_amd as va
+from speculative_tree_verify_mla_amd import binding
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "verify_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(verify_attn_\w+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding_list():
+    assert _declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = va.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.verify_attn_plan_struct_size() == ctypes.sizeof(binding.VaPlan)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        binding.load_library(tmp_path / "nope.so")
+
+
+def test_error_strings():
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8]:
+        s = va.verify_attn_error_string(code)
+        assert s and s != "unknown error code"
+    assert va.verify_attn_error_string(-99) == "unknown error code"
+
+
+# --------------------------------------------------------------------------- plan
+def _plan(H, L, T, cus=256):
+    return va.verify_attn_plan(H, L, T, num_cus=cus)
+
+
+def test_plan_long_prefix_h8_t16():
+    p = _plan(8, [65536], [16])
+    assert p.magic == binding.VA_PLAN_MAGIC and p.rows_per_group == 64 and p.tile_keys == 32
+    assert p.num_groups[0] == 2                     # 128 rows / 64
+    # keys x groups spread over 256 CUs: 2 * 65552 / 256 = 512 keys per work item
+    assert p.nsplit[0] == 128
+    assert p.total_work == 256
+    assert p.total_tree == 16 and p.total_rows == 128
+    o = 256 * 64 * 512 * 4
+    assert p.lse_offset == o
+    assert p.status_offset == o + 256 * 64 * 4
+    assert p.workspace_bytes == o + 256 * 64 * 4 + 1024
+
+
+def test_plan_full_heads_and_ragged_batch():
+    p = _plan(64, [200000], [16])
+    assert p.num_groups[0] == 16 and p.nsplit[0] == 16 and p.total_work == 256
+    p = _plan(16, [1024, 16384, 65536, 131072], [32] * 4)
+    assert [p.num_groups[r] for r in range(4)] == [8] * 4
+    keys = [1024 + 32, 16384 + 32, 65536 + 32, 131072 + 32]
+    per = -(-8 * sum(keys) // 256)
+    assert p.splits() == [-(-k // per) for k in keys]
+    assert p.work_begin[4] == p.total_work == 8 * sum(p.splits())
+    assert [p.tree_begin[r] for r in range(5)] == [0, 32, 64, 96, 128]
+
+
+def test_plan_small_inputs_keep_a_minimum_split_length():
+    p = _plan(8, [256], [4])
+    assert p.num_groups[0] == 1 and p.nsplit[0] == 2      # 260 keys, >= 256 per split
+    p = _plan(1, [0], [1])
+    assert p.nsplit[0] == 1 and p.total_work == 1 and p.total_rows == 1
+
+
+def test_plan_split_count_is_capped():
+    p = _plan(1, [10_000_000], [1], cus=100000)
+    assert p.nsplit[0] == binding.VA_MAX_SPLITS
+
+
+def test_plan_env_override(monkeypatch):
+    monkeypatch.setenv("VA_NSPLIT", "7")
+    p = _plan(8, [65536], [16])
+    assert p.nsplit[0] == 7 and p.total_work == 14
+    monkeypatch.setenv("VA_NSPLIT", "100000")
+    p = _plan(8, [100], [16])
+    assert p.nsplit[0] == 4                                # capped at ceil(116 / 32) tiles
+
+
+@pytest.mark.parametrize("H,L,T", [(0, [10], [4]), (8, [10], [0]), (8, [10], [65]),
+                                   (8, [-1], [4]), (2000, [10], [4])])
+def test_plan_rejects_bad_shapes(H, L, T):
+    with pytest.raises(va.VerifyAttnError) as e:
+        _plan(H, L, T)
+    assert e.value.code == -2
+
+
+def test_plan_rejects_too_many_requests_and_nulls():
+    with pytest.raises(va.VerifyAttnError) as e:
+        _plan(8, [10] * 65, [4] * 65)
+    assert e.value.code == -2
+    lib = va.load_library()
+    plan = binding.VaPlan()
+    assert lib.verify_attn_plan(1, 8, None, None, 256, ctypes.byref(plan), None) == -1
+
+
+# --------------------------------------------------------------------------- host-side run checks
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def _run(lib, plan, q=4096, kv=8192, num_slots=100, stride=576, tab=64, ind=64, pl=64, par=64,
+         ws=1 << 20, ws_bytes=None):
+    ws_bytes = plan.workspace_bytes if ws_bytes is None else ws_bytes
+    return lib.verify_attn_run(ctypes.byref(plan), _fake(q), _fake(kv), num_slots, stride,
+                               _fake(tab), 1000, _fake(ind), _fake(pl), _fake(par), 0.1, _fake(ws),
+                               ws_bytes, None)
+
+
+def test_run_argument_errors_are_caught_before_launch():
+    lib = va.load_library()
+    plan = _plan(8, [100], [4])
+    assert _run(lib, plan, q=0) == -1
+    assert _run(lib, plan, tab=0) == -1
+    assert _run(lib, plan, q=4098) == -3                  # misaligned q
+    assert _run(lib, plan, kv=8200) == -3                 # misaligned pool
+    assert _run(lib, plan, stride=580) == -3              # stride not a multiple of 8
+    assert _run(lib, plan, stride=512) == -2              # stride below 576
+    assert _run(lib, plan, num_slots=0) == -2
+    assert _run(lib, plan, ws=0) == -4
+    assert _run(lib, plan, ws=(1 << 20) + 16) == -4       # not 256-byte aligned
+    assert _run(lib, plan, ws_bytes=plan.workspace_bytes - 1) == -4
+    bad = binding.VaPlan()
+    ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
+    bad.magic = 0
+    assert _run(lib, bad) == -5
+    assert lib.verify_attn_reduce(ctypes.byref(bad), _fake(1 << 20), _fake(4096), _fake(4096),
+                                  None) == -5
+    assert lib.verify_attn_reduce(ctypes.byref(plan), _fake(1 << 20), _fake(4100), _fake(4096),
+                                  None) == -3
+    assert lib.verify_attn_gather_rows(_fake(4096), 10, 576, _fake(64), -1, _fake(4096),
+                                       None) == -2
+    assert lib.verify_attn_gather_rows(_fake(4096), 10, 576, _fake(64), 0, _fake(4096),
+                                       None) == 0
+
+
+@pytest.mark.parametrize("parent,ok", [([-1], True), ([-1, 0, 1, 0, -1], True), ([0], False),
+                                       ([-1, 1], False), ([-1, -2], False), ([-1] * 65, False)])
+def test_check_tree(parent, ok):
+    assert (va.verify_attn_check_tree(parent) == 0) == ok

@@ -1,0 +1,389 @@
+"""GPU parity of the HIP verify path against the CPU fp64 oracle.
+
+Every test calls the C ABI through the thin binding and compares element by
+element with the oracle on the same seeded inputs.  Tolerances: max abs error
+1e-2 on the bf16 output and 1e-3 on the fp32 LSE.  Gathers, permuted pools,
+graph replays and repeated calls are compared bit for bit.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_tree_verify_mla_amd as va
+from speculative_tree_verify_mla_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _bf16(a):
+    return _t(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+class Dev:
+    """Device copies of a workload."""
+
+    def __init__(self, wl, kv_pool=None):
+        self.wl = wl
+        self.q = _bf16(wl.q)
+        self.kv = kv_pool if kv_pool is not None else _bf16(wl.kv_pool)
+        self.table = _t(wl.slot_table)
+        self.indptr = _t(wl.slot_indptr)
+        self.prefix = _t(wl.prefix_len)
+        self.parent = _t(wl.parent)
+
+
+def run_gpu(wl, d=None, plan=None, prefix_host=None):
+    d = d or Dev(wl)
+    plan = plan or va.verify_attn_plan(wl.num_heads, wl.prefix_len if prefix_host is None
+                                       else prefix_host, wl.num_tree)
+    ws = va.workspace_for(plan, DEV)
+    out, lse = va.verify_attn(d.q, d.kv, d.table, d.indptr, d.prefix, d.parent, wl.sm_scale,
+                              num_tree=wl.num_tree, prefix_len_host=wl.prefix_len, plan=plan,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    status = va.verify_attn_read_status(plan, ws)
+    return out, lse, status, plan
+
+
+def bf16_representation_error(ref):
+    """|round_bf16(x) - x|: what any bf16 output must carry at the exact value x."""
+    r32 = ref.astype(np.float32)
+    rb = inputs.bf16_to_f32(inputs.bf16_bits(r32)).astype(np.float64)
+    return np.abs(rb - ref)
+
+
+def check(wl, out, lse, rows=None, what="", raw=False):
+    """Compare with the oracle.  The output bound is 1e-2 beyond the bf16
+    representation error of the exact value (which alone reaches 7.8e-3 at
+    2 <= |o| < 4 and 1.6e-2 at 4 <= |o| < 8); with raw=True the plain
+    max |out - oracle| <= 1e-2 is required as well."""
+    ref, ref_lse = oracle.verify_attn_workload(wl, rows=rows)
+    got = out.float().cpu().numpy().reshape(-1, 512).astype(np.float64)
+    gl = lse.cpu().numpy().reshape(-1)
+    ref = ref.reshape(-1, 512)
+    ref_lse = ref_lse.reshape(-1)
+    sel = np.arange(got.shape[0]) if rows is None else np.asarray(sorted(rows))
+    diff = np.abs(got[sel] - ref[sel])
+    e = diff.max()
+    beyond = (diff - bf16_representation_error(ref[sel])).max()
+    el = np.abs(gl[sel] - ref_lse[sel]).max()
+    say(f"  {what} rows={len(sel)} max|out-oracle|={e:.3e} (beyond bf16 rounding {beyond:.3e}) "
+        f"max|lse-oracle|={el:.3e} max|oracle|={np.abs(ref[sel]).max():.2f}")
+    assert np.isfinite(got[sel]).all() and np.isfinite(gl[sel]).all()
+    assert beyond <= OUT_TOL, beyond
+    if raw:
+        assert e <= OUT_TOL, e
+    assert el <= LSE_TOL, el
+    return e, el
+
+
+def sample_rows(wl, per_group=2, seed=0):
+    """A spread of rows: both ends of every 64-row group, plus random ones."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    base = 0
+    H = wl.num_heads
+    for T in wl.num_tree:
+        n = int(T) * H
+        for g0 in range(0, n, 64):
+            g1 = min(n, g0 + 64)
+            rows.update([base + g0, base + g1 - 1])
+            rows.update((base + rng.integers(g0, g1, size=per_group)).tolist())
+        base += n
+    return sorted(rows)
+
+
+# --------------------------------------------------------------------------- the five workloads
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_config_parity_all_rows(idx):
+    wl = inputs.make_config(idx)
+    say(f"config {idx} {wl.name}: H={wl.num_heads} T={wl.num_tree.tolist()} "
+        f"L={wl.prefix_len.tolist()}")
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0
+    say(f"  nsplit={plan.splits()} work={plan.total_work}")
+    check(wl, out, lse, what=f"config {idx}", raw=True)
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_config_parity_sampled_rows(idx):
+    wl = inputs.make_config(idx)
+    say(f"config {idx} {wl.name}: H={wl.num_heads} T={wl.num_tree.tolist()} "
+        f"L={wl.prefix_len.tolist()}")
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0
+    say(f"  nsplit={plan.splits()} work={plan.total_work}")
+    check(wl, out, lse, rows=sample_rows(wl), what=f"config {idx}", raw=True)
+    # every row: finite, and lse at least the log of the prefix length
+    o = out.float()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+# --------------------------------------------------------------------------- shapes and edges
+EDGE = [
+    # (H, T list, L list, tree)
+    (1, [1], [0], "random"),
+    (1, [1], [1], "random"),
+    (3, [5], [1], "random"),
+    (8, [16], [31], "random"),
+    (8, [16], [32], "random"),
+    (8, [16], [33], "random"),
+    (5, [13], [100], "random"),
+    (8, [4], [0], "chain"),
+    (64, [64], [7], "random"),
+    (16, [64], [1000], "star"),
+    (2, [64], [300], "chain"),
+    (7, [3, 17, 1, 64], [0, 45, 513, 2000], "random"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"H{c[0]}_T{c[1]}_L{c[2]}_{c[3]}")
+def test_edge_shapes(case):
+    H, T, L, tree = case
+    wl = inputs.make_workload("edge", H, T, L, 4096, seed=sum(L) + H, tree=tree,
+                              table="interleaved" if len(T) > 1 else "scattered")
+    say(f"edge H={H} T={T} L={L} {tree}")
+    out, lse, status, _ = run_gpu(wl)
+    assert status == 0
+    check(wl, out, lse, what="edge")
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 3, 7, 64, 129])
+def test_split_count_does_not_change_the_result(nsplit, monkeypatch):
+    wl = inputs.make_workload("ns", 8, [16], [4096], 16384, seed=3)
+    monkeypatch.setenv("VA_NSPLIT", str(nsplit))
+    say(f"VA_NSPLIT={nsplit}")
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0 and plan.nsplit[0] == nsplit
+    check(wl, out, lse, what=f"nsplit {nsplit}")
+
+
+def test_graph_bound_above_actual_prefix():
+    """Plan with an upper bound, run with a shorter device prefix length."""
+    wl = inputs.make_workload("bound", 8, [16], [3000], 8192, seed=5)
+    say("plan for L<=5000, run L=3000")
+    out, lse, status, plan = run_gpu(wl, prefix_host=[5000])
+    assert status == 0
+    check(wl, out, lse, what="bound")
+
+
+# --------------------------------------------------------------------------- coverage closed forms
+@pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000])
+def test_zero_query_counts_every_visible_key(L):
+    """q = 0: lse = ln(number of visible keys) exactly; one key more or less
+    moves it by >= 1e-3 at these lengths."""
+    H, T = 4, 16
+    wl = inputs.make_workload("q0", H, [T], [L], 4096, seed=100 + L,
+                              q_override=np.zeros((T, H, 576), dtype=np.uint16))
+    say(f"q=0 L={L}")
+    out, lse, status, _ = run_gpu(wl)
+    assert status == 0
+    vis = oracle.tree_visibility(wl.parent)
+    expect = np.log(L + vis.sum(1))
+    got = lse.cpu().numpy()
+    assert np.abs(got - expect[:, None]).max() <= LSE_TOL
+    check(wl, out, lse, what="q=0")
+
+
+def _needle(L, T, key, seed):
+    H = 2
+    wl = inputs.make_workload("needle", H, [T], [L], 4 * (L + T) + 64, seed=seed)
+    wl.q = inputs.bf16_bits(np.full((T, H, 576), 0.5, dtype=np.float32))
+    wl.kv_pool = wl.kv_pool.copy()
+    wl.kv_pool[wl.slot_table[key]] = inputs.bf16_bits(
+        np.linspace(-3.0, 3.0, 576, dtype=np.float32) * 0.25 + 4.0)
+    return wl
+
+
+@pytest.mark.parametrize("nsplit", [1, 5])
+def test_needle_at_tile_and_split_edges(nsplit, monkeypatch):
+    """A dominant key at every tile/split edge must reach every node's output."""
+    L, T = 2000, 16
+    monkeypatch.setenv("VA_NSPLIT", str(nsplit))
+    per_split = -(-(L + T) // nsplit)
+    chunk = -(-per_split // 32) * 32                       # split length in keys
+    keys = sorted(set([0, 1, 30, 31, 32, 33, 63, 64, L - 1] +
+                      [c + d for c in range(0, L, chunk) for d in (-1, 0) if 0 <= c + d < L]))
+    for key in keys:
+        wl = _needle(L, T, key, seed=7)
+        out, lse, status, _ = run_gpu(wl)
+        assert status == 0
+        v = inputs.bf16_to_f32(wl.kv_pool[wl.slot_table[key]])[:512]
+        err = np.abs(out.float().cpu().numpy() - v).max()
+        say(f"  needle key={key} nsplit={nsplit} max|out-v|={err:.3e}")
+        assert err <= OUT_TOL
+
+
+def test_needle_on_draft_nodes_respects_the_tree():
+    L, T = 700, 32
+    base = inputs.make_workload("nd", 2, [T], [L], 4 * (L + T) + 64, seed=9)
+    vis = oracle.tree_visibility(base.parent)
+    for j in range(T):
+        wl = _needle(L, T, L + j, seed=9)
+        out, lse, status, _ = run_gpu(wl)
+        assert status == 0
+        v = inputs.bf16_to_f32(wl.kv_pool[wl.slot_table[L + j]])[:512]
+        got = out.float().cpu().numpy()
+        for i in range(T):
+            near = np.abs(got[i] - v).max() <= OUT_TOL
+            assert near == bool(vis[i, j]), (i, j)
+        check(wl, out, lse, what=f"draft needle {j}")
+
+
+# --------------------------------------------------------------------------- bit-exactness
+def test_permuted_pool_gives_identical_bits():
+    wl = inputs.make_workload("perm", 8, [16], [5000], 16384, seed=13)
+    out, lse, _, _ = run_gpu(wl)
+    pi = np.random.default_rng(1).permutation(wl.num_slots)
+    pool2 = np.empty_like(wl.kv_pool)
+    pool2[pi] = wl.kv_pool
+    wl2 = inputs.Workload(**{**wl.__dict__, "kv_pool": pool2,
+                             "slot_table": pi[wl.slot_table].astype(np.int32)})
+    out2, lse2, _, _ = run_gpu(wl2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_unused_slots_poisoned_with_nan_are_never_read():
+    wl = inputs.make_workload("poison", 8, [16], [3000], 8192, seed=17)
+    out, lse, _, _ = run_gpu(wl)
+    pool = wl.kv_pool.copy()
+    unused = np.setdiff1d(np.arange(wl.num_slots), wl.slot_table)
+    pool[unused] = 0x7FC0
+    d = Dev(wl, kv_pool=_bf16(pool))
+    out2, lse2, status, _ = run_gpu(wl, d=d)
+    assert status == 0
+    assert torch.isfinite(out2.float()).all()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_repeated_calls_are_bitwise_identical():
+    wl = inputs.make_workload("rep", 8, [16], [10000], 16384, seed=19)
+    d = Dev(wl)
+    a, la, _, plan = run_gpu(wl, d=d)
+    for _ in range(3):
+        b, lb, _, _ = run_gpu(wl, d=d, plan=plan)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(la.view(torch.int32), lb.view(torch.int32))
+
+
+def test_padded_row_stride_matches_dense_pool():
+    wl = inputs.make_workload("stride", 4, [8], [900], 2048, seed=23)
+    out, lse, _, _ = run_gpu(wl)
+    wide = np.full((wl.num_slots, 640), 0x7FC0, dtype=np.uint16)
+    wide[:, :576] = wl.kv_pool
+    kv_wide = _bf16(wide)
+    d = Dev(wl, kv_pool=kv_wide)
+    assert kv_wide.stride(0) == 640
+    out2, lse2, status, _ = run_gpu(wl, d=d)
+    assert status == 0
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_gather_rows_is_bit_exact():
+    rng = np.random.default_rng(29)
+    pool = inputs.normal_bf16(rng, (5000, 576))
+    table = rng.choice(5000, size=3001, replace=True).astype(np.int32)
+    table[[5, 700]] = [-1, 5000]                              # invalid slots -> NaN rows
+    dst = torch.empty((3001, 576), dtype=torch.bfloat16, device=DEV)
+    va.verify_attn_gather_rows(_bf16(pool), _t(table), 3001, dst)
+    torch.cuda.synchronize()
+    got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+    ok = np.ones(3001, dtype=bool)
+    ok[[5, 700]] = False
+    np.testing.assert_array_equal(got[ok], pool[table[ok]])
+    assert (got[~ok] == 0x7FC0).all()
+
+
+def test_graph_capture_replays_bit_exact_and_follows_device_lengths():
+    wl = inputs.make_workload("graph", 8, [16], [6000], 16384, seed=31)
+    d = Dev(wl)
+    plan = va.verify_attn_plan(8, [6000], [16])
+    ws = va.workspace_for(plan, DEV)
+    out = torch.empty((16, 8, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((16, 8), dtype=torch.float32, device=DEV)
+    eager_o, eager_l = va.verify_attn(d.q, d.kv, d.table, d.indptr, d.prefix, d.parent,
+                                      wl.sm_scale, num_tree=[16], prefix_len_host=[6000],
+                                      plan=plan, workspace=ws)
+    eager_o, eager_l = eager_o.clone(), eager_l.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            va.verify_attn(d.q, d.kv, d.table, d.indptr, d.prefix, d.parent, wl.sm_scale,
+                           num_tree=[16], prefix_len_host=[6000], plan=plan, workspace=ws,
+                           out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.zero_()
+        torch.randn(1 << 20, device=DEV).sum().item()           # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        assert torch.equal(out.view(torch.int16), eager_o.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), eager_l.view(torch.int32))
+    # shorter prefix through the device length only
+    d.prefix.fill_(2500)
+    g.replay()
+    torch.cuda.synchronize()
+    # the kernel now reads entries 0..2515 of the unchanged table: 2500 prefix
+    # keys, then the draft nodes at entries 2500..2515
+    wl3 = inputs.Workload(**{**wl.__dict__, "prefix_len": np.array([2500], np.int32),
+                             "slot_table": wl.slot_table[:2516].copy(),
+                             "slot_indptr": np.array([0, 2516], np.int32)})
+    check(wl3, out, lse, what="replay L=2500")
+
+
+# --------------------------------------------------------------------------- device-data errors
+def test_device_data_errors_poison_only_their_request():
+    wl = inputs.make_workload("err", 4, [8, 8], [300, 200], 4096, seed=37, table="interleaved")
+    good_o, good_l, status, plan = run_gpu(wl)
+    assert status == 0
+    cases = []
+    t = wl.slot_table.copy()
+    t[10] = wl.num_slots + 5                                    # request 0, bad slot
+    cases.append(("slot", dict(slot_table=t), 4))
+    p = wl.parent.copy()
+    p[3] = 5                                                    # request 0, parent >= i
+    cases.append(("parent", dict(parent=p), 8))
+    ind = wl.slot_indptr.copy()
+    ind[1] = ind[1] - 5                                         # request 0 table too short
+    cases.append(("short", dict(slot_indptr=ind), 2))
+    for name, change, bit in cases:
+        w2 = inputs.Workload(**{**wl.__dict__, **change})
+        d = Dev(w2)
+        o, l, status, _ = run_gpu(w2, d=d, plan=plan)
+        say(f"  error case {name}: status={status}")
+        assert status & bit
+        of = o.float()
+        assert torch.isnan(of[:8]).all() and torch.isnan(l[:8]).all()
+        if name != "short":
+            assert torch.equal(o[8:].view(torch.int16), good_o[8:].view(torch.int16))
+    # device prefix above the planned bound
+    d = Dev(wl)
+    d.prefix[1] = 250
+    o, l, status, _ = run_gpu(wl, d=d, plan=plan)
+    assert status & 1
+    assert torch.isnan(o[8:].float()).all()
+    assert torch.equal(o[:8].view(torch.int16), good_o[:8].view(torch.int16))
