@@ -3,29 +3,50 @@
 // Split-KV partial pass + log-sum-exp reduce ("The Verify Kernel
 // Breakthrough", section "The Message in Context": partial+reduce;
 // "The Architecture Detective", section "The Split Verify Design": LSE
-// merge), with the KV tile loaded once and shared by every head and draft
+// merge), with each KV tile loaded once and shared by every head and draft
 // node of a row group ("The Execution Phase", section "The Core Design: A
 // Streaming Flash Attention Kernel": KV-tile outer, heads inner), 16-byte
 // gathers of the page_size=1 rows (same page, section "The Optimization That
 // Unlocked 3-6x Speedup": 128-bit loads) and graph-capture-safe launches
 // (same page, section "Making the Kernel CUDA Graph Capture-Safe").
 //
-// gfx950 mapping of one work item (request r, row group g, KV split s):
-//   - 256 threads = 4 wave64s; each wave owns 16 query rows (node, head).
-//   - Per 32-key tile the block gathers 32 pool rows (72 x 16 B each) into
-//     LDS twice: row-major K[key][576] for the score contraction and a
-//     transposed V^T[col][key] (8x8 register transposes) for the value
-//     contraction, so both MFMA operands are single 16-byte LDS reads.
-//   - S^T[key][row] = K . Q^T on v_mfma_f32_16x16x32_bf16 (A = K tile from
-//     LDS, B = the wave's Q rows held in VGPRs).  The MFMA output layout puts
-//     one query row per lane (lane % 16), so the online softmax needs only
-//     two cross-lane steps per tile and the probabilities are already the B
-//     operand of O^T[col][row] = V^T . P^T (keys reordered consistently on
-//     both operands).
+// gfx950 mapping of one work item (request r, row group g of 64 query rows,
+// KV split s):
+//   - 256 threads = 4 wave64s.  Wave w owns rows 32*(w&1) .. +31 of the row
+//     group (two 16-row MFMA blocks, so every 16-byte LDS fragment feeds two
+//     MFMAs and the LDS read rate matches the MFMA rate) and half h = w>>1 of
+//     the work: the score columns 288*h .. +287 and the output columns
+//     256*h .. +255.  The two waves of a row half add their partial scores
+//     through LDS, then both run the same softmax on the full scores.
+//   - Tiles of 32 pool rows go straight from HBM into LDS with
+//     global_load_lds_dwordx4 (1 KB per wave instruction), triple-buffered:
+//     the next two tiles are in flight while one is consumed.  Slot indices
+//     are fetched a tile ahead of their rows.  The latent part of a row is
+//     stored with a 1072-byte pitch and the rope part XOR-swizzled, so both
+//     MFMA read patterns below are free of LDS bank conflicts.
+//   - S^T[key][row] = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K fragment
+//     from LDS, B = Q rows held in VGPRs; the 32x32 shape runs near the
+//     dense bf16 peak, the 16x16 one at about a third of it).  The output
+//     layout gives each lane one query row (lane % 32) and 16 of its 32
+//     keys, so the row max needs one cross-lane step, and the probabilities
+//     of keys 16*ks .. +15 are already, register for register, the B operand
+//     of O^T = V^T . P^T for k-step ks.  That operand's A side comes from the
+//     same K tile through ds_read_b64_tr_b16 (transpose reads: no transposed
+//     copy of V).
+//   - Each row's probabilities are taken against a fixed reference: the
+//     row's first finite tile max.  Probabilities may then exceed 1 (up to
+//     2^64), which bf16 and the fp32 accumulators hold without loss of
+//     relative precision, and the accumulators are never rescaled, so they
+//     stay in the MFMA accumulator registers for the whole pass.  If a later
+//     tile beats a row's reference by more than 2^64 (only adversarial
+//     inputs do), the work item restarts from its first tile with the
+//     reference raised to the largest max seen.
 //   - The tree mask is one 64-bit ancestor mask per draft node, built in the
-//     prologue from parent[]; only draft positions (>= L) consult it.
-//   - Each work item writes o/l (fp32) and lse (base 2) for its rows; the
-//     reduce merges a row's splits and writes bf16 out and natural-log lse.
+//     prologue from parent[]; only tiles reaching past the prefix consult it.
+//   - Each work item writes its unnormalised accumulators in the MFMA output
+//     layout (1 KB per wave store), lse (base 2) and the sum of its bf16
+//     weights per row; the reduce normalises, merges a row's splits and
+//     writes bf16 out and natural-log lse.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -37,22 +58,34 @@
 
 namespace {
 
-constexpr int DQK = VA_D_QK;   // 576
-constexpr int DV = VA_D_V;     // 512
-constexpr int TILE = 32;       // keys per tile
-constexpr int THREADS = 256;   // 4 waves
-constexpr int ROWS = 64;       // query rows per work item (16 per wave)
-constexpr int KS_STRIDE = DQK + 8;   // bf16 per K row in LDS (1168 B: conflict-free 16-row reads)
-constexpr int VT_STRIDE = TILE + 8;  // bf16 per V^T row in LDS (80 B)
-constexpr int QK_STEPS = DQK / 32;   // 18 MFMA k-steps for the score
-constexpr int O_BLOCKS = DV / 16;    // 32 MFMA column blocks for the output
+constexpr int DQK = VA_D_QK;      // 576
+constexpr int DV = VA_D_V;        // 512: value columns = latent columns
+constexpr int DROPE = DQK - DV;   // 64 rope columns
+constexpr int TILE = 32;          // keys per LDS tile
+constexpr int THREADS = 256;      // 4 waves
+constexpr int ROWS = 64;          // query rows per work item
+constexpr int LAT_STRIDE = DV + 24;               // bf16 per latent row in LDS (1072 B)
+constexpr int LAT_ELEMS = TILE * LAT_STRIDE;
+constexpr int BUF_ELEMS = LAT_ELEMS + TILE * DROPE;  // one tile buffer: 38,400 B
+constexpr int QK_STEPS = DQK / 16;   // 36 MFMA k-steps (16 columns each) for the score
+constexpr int QK_HALF = QK_STEPS / 2; // 18 of them per wave
+constexpr int LAT_STEPS = DV / 16;   // the first 32 are latent columns, the last 4 rope
+constexpr int O_HALF = DV / 32 / 2;  // 8 MFMA column blocks (32 columns) of the output per wave
+constexpr int PART_VEC = ROWS * DV / 4;  // float4 entries of one work item's partial output
+constexpr int DMA_PER_TILE = TILE / 4 + 1;  // per wave: 8 latent rows + 1 block of 8 rope rows
 constexpr int MIN_KEYS_PER_SPLIT = 256;
+constexpr float REF_SLACK = 64.f;  // log2 units: probabilities stay <= 2^64
+constexpr int MAX_PASSES = 8;      // restarts of a work item with a raised reference
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct PartialArgs {
   const uint16_t* q;
@@ -61,34 +94,41 @@ struct PartialArgs {
   int32_t stride;
   int32_t num_requests;
   int32_t num_heads;
+  int32_t total_work;
   float scale_log2;   // sm_scale * log2(e): scores are kept in base 2
   const int32_t* slot_table;
   int32_t slot_table_len;
   const int32_t* slot_indptr;
   const int32_t* prefix_len;
   const int32_t* parent;
-  float* part_o;      // [work][ROWS][DV]
-  float* part_lse;    // [work][ROWS]
+  float* part_o;      // [work][PART_VEC] f32x4, unnormalised, MFMA layout (see the reduce)
+  float* part_lse;    // [work][ROWS][2]: lse (base 2), sum of bf16 weights
   uint32_t* status;   // [work]
   int32_t num_tree[VA_MAX_REQUESTS];
   int32_t max_prefix[VA_MAX_REQUESTS];
   int32_t nsplit[VA_MAX_REQUESTS];
+  int32_t num_groups[VA_MAX_REQUESTS];
   int32_t tree_begin[VA_MAX_REQUESTS + 1];
   int32_t work_begin[VA_MAX_REQUESTS + 1];
 };
 
 struct ReduceArgs {
   const float* part_o;
-  const float* part_lse;
+  const float* part_lse;   // [work][ROWS][2]: lse (base 2), sum of bf16 weights
   const uint32_t* status;
   uint16_t* out;
   float* lse;
   int32_t num_requests;
   int32_t num_heads;
   int32_t nsplit[VA_MAX_REQUESTS];
+  int32_t num_groups[VA_MAX_REQUESTS];
   int32_t tree_begin[VA_MAX_REQUESTS + 1];
   int32_t work_begin[VA_MAX_REQUESTS + 1];
 };
+
+// Source of the pieces of keys that are missing (past the split end) or
+// whose slot is outside the pool: a row of zeros.
+__device__ const uint16_t va_zero_row[DQK] = {};
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -98,54 +138,80 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
-// One 16-byte piece (8 bf16 columns starting at col8*8) of pool row `slot`.
-// Slots outside the pool are never dereferenced: *ok is cleared and zeros
-// are returned.
-__device__ __forceinline__ u32x4 gather16(const uint16_t* __restrict__ kv, int64_t num_slots,
-                                          int32_t stride, int32_t slot, int col8, bool* ok) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (slot >= 0 && (int64_t)slot < num_slots) {
-    v = *reinterpret_cast<const u32x4*>(kv + (int64_t)slot * stride + col8 * 8);
-  } else {
-    *ok = false;
-  }
-  return v;
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-// Key of a tile that loader quad kq stages as its j-th row (j = 0..7).  The
-// same order is the key order of the value contraction: V^T slot 8*kq + j
-// holds this key, and the lane group kq of the score MFMA output holds keys
-// 4*kq + i (first 16-key block) and 16 + 4*kq + i (second block).
-__device__ __forceinline__ int stage_key(int kq, int j) {
-  return j < 4 ? 4 * kq + j : 16 + 4 * kq + (j - 4);
+// Asynchronous copy of 16 bytes per lane from global memory into LDS: lane i
+// writes lds_base + 16*i (global_load_lds_dwordx4; lds_base is wave-uniform).
+__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane block,
+// lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
+// i/4, i/4+4, i/4+8 and i/4+12.  A block whose lane i addresses
+// K[k0 + i/4][c0 + 4*(i%4)] therefore hands lane i the column c0 + i of the
+// four keys k0..k0+3: half of a value-MFMA operand, read from the row-major
+// key tile without a transposed copy.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// Table entry of logical key k with the index clamped into [0, k_end) so the
+// load stays inside the request's table (k_end >= 1).
+__device__ __forceinline__ int32_t table_entry(const int32_t* __restrict__ table, int k,
+                                               int k_end) {
+  return table[k < k_end ? k : k_end - 1];
+}
+
+// Rope columns of a key row are stored as 8 pieces of 16 bytes whose order
+// is XOR-swizzled by the key index, spreading 16 consecutive keys over all
+// LDS banks for the score MFMA reads.
+__device__ __forceinline__ int rope_piece(int key, int piece) { return piece ^ ((key >> 1) & 7); }
 
 __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[TILE * KS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[DV * VT_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[3 * BUF_ELEMS];
+  __shared__ f32x4 xs[2][2][4][64];   // partial scores [row half][half][register quad][lane]
   __shared__ uint64_t anc[VA_MAX_TREE];
   __shared__ uint32_t status_sh;
+  __shared__ uint32_t restart_sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int lrow = lane & 15;   // MFMA column index: this lane's query row
-  const int lgrp = lane >> 4;   // MFMA k-group of this lane
-  const int w = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wave & 1;      // row half of the work item's 64 rows
+  const int hf = wave >> 1;     // score-column half and output-column half
+  const int lrow = lane & 31;   // MFMA column: this lane's query row within the row half
+  const int lh = lane >> 5;     // MFMA k-half of this lane (keys 4*lh + 8*j + i of a tile)
 
-  // ---- decode the work item: request r, row group g, split s
+  // Work items are ordered (request, split, row group); block b runs on XCD
+  // b % 8, so each XCD takes a contiguous run of work items and the row
+  // groups that read the same KV split share that XCD's L2.
+  const int per_xcd = (a.total_work + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= a.total_work) return;
+
   int r = 0;
   while (r + 1 < a.num_requests && a.work_begin[r + 1] <= w) ++r;
-  const int ns = a.nsplit[r];
+  const int G = a.num_groups[r];
   const int local = w - a.work_begin[r];
-  const int g = local / ns;
-  const int s = local - g * ns;
+  const int s = local / G;
+  const int g = local - s * G;
+  const int ns = a.nsplit[r];
   const int T = a.num_tree[r];
   const int H = a.num_heads;
   const int rows_r = T * H;
 
   if (tid == 0) status_sh = 0u;
-  __syncthreads();
 
   uint32_t st = 0u;
   int L = a.prefix_len[r];
@@ -156,15 +222,17 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
   const int n = L + T;
   const int tab0 = a.slot_indptr[r];
   const int tab1 = a.slot_indptr[r + 1];
-  int n_read = n;   // keys whose table entry exists
+  int n_valid = n;   // keys whose table entry exists
   if (tab0 < 0 || tab1 < tab0 || tab1 > a.slot_table_len || tab1 - tab0 < n) {
     st |= VA_STATUS_SHORT_TABLE;
-    n_read = (tab0 < 0 || tab1 < tab0 || tab0 >= a.slot_table_len)
-                 ? 0 : min(tab1, a.slot_table_len) - tab0;
+    n_valid = (tab0 < 0 || tab1 < tab0 || tab0 >= a.slot_table_len)
+                  ? 0 : min(min(tab1, a.slot_table_len) - tab0, n);
   }
   const int chunk = ((n + ns - 1) / ns + TILE - 1) / TILE * TILE;
   const int k0 = s * chunk;
-  const int k1 = min(n, k0 + chunk);
+  const int k1 = min(n_valid, k0 + chunk);   // end of this split (keys past a short table dropped)
+  const int ntiles = k1 > k0 ? (k1 - k0 + TILE - 1) / TILE : 0;
+  const int32_t* table = a.slot_table + (n_valid > 0 ? tab0 : 0);
 
   // ---- ancestor masks (bit j of anc[i]: draft node j is i or an ancestor of i)
   if (tid < VA_MAX_TREE) {
@@ -185,221 +253,418 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     anc[tid] = m;
   }
 
-  // ---- this lane's query row and its Q fragment (B operand of the score MFMA)
-  const int rho = g * ROWS + wave * 16 + lrow;
+  // ---- Q fragments of this lane's row over this wave's 288 score columns
+  const int rho = g * ROWS + rh * 32 + lrow;
   const bool row_ok = rho < rows_r;
-  bf16x8 qf[QK_STEPS];
+  bf16x8 qf[QK_HALF];
   {
     const int64_t qrow = (int64_t)a.tree_begin[r] * H + (row_ok ? rho : 0);
-    const uint16_t* qp = a.q + qrow * DQK + lgrp * 8;
+    const uint16_t* qp = a.q + qrow * DQK + hf * (QK_HALF * 16) + lh * 8;
 #pragma unroll
-    for (int k = 0; k < QK_STEPS; ++k) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + k * 32);
+    for (int k = 0; k < QK_HALF; ++k) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + k * 16);
+      if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
       qf[k] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  __syncthreads();   // anc[] ready
-  const uint64_t anc_row = row_ok ? anc[rho / H] : 0ull;
 
-  // ---- loader roles: quad kq = tid & 3 stages 8 keys x latent block fb;
-  //      every thread also stages one 16-byte rope piece.
-  const int kq = tid & 3;
-  const int fb = tid >> 2;        // 0..63: latent columns fb*8 .. fb*8+7
-  const int rkey = tid >> 3;      // rope piece: key 0..31
-  const int rcol = 64 + (tid & 7);  // 16-byte column index 64..71 (cols 512..575)
-  const int32_t* table = a.slot_table + (tab0 < 0 ? 0 : tab0);
-
-  u32x4 lat[8];
-  u32x4 rope;
-  bool ok = true;
-  auto load_tile = [&](int kt) {
+  // ---- tile loader: this wave moves keys 8*wave .. +7 of a tile: 8 latent
+  // rows (one 1 KB DMA each) and their rope parts (one DMA of 8 x 128 B).
+  uint32_t bad = 0u;
+  auto load_slot = [&](int t) -> int32_t {
+    return table_entry(table, k0 + t * TILE + wave * 8 + (lane & 7), k1);
+  };
+  auto issue_tile = [&](int t, int32_t vslot, uint16_t* buf) {
+    const int k = k0 + t * TILE + wave * 8 + (lane & 7);
+    const bool exists = k < k1;
+    const bool inside = vslot >= 0 && (int64_t)vslot < a.num_slots;
+    if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
+    const uint64_t use = __ballot(exists && inside);   // bit j: key 8*wave + j is read
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int k = kt + stage_key(kq, j);
-      lat[j] = u32x4{0u, 0u, 0u, 0u};
-      if (k < n && k < n_read) lat[j] = gather16(a.kv, a.num_slots, a.stride, table[k], fb, &ok);
+      const int32_t sj = __builtin_amdgcn_readlane(vslot, j);
+      const uint16_t* row = ((use >> j) & 1ull) ? a.kv + (int64_t)sj * a.stride : va_zero_row;
+      dma16(row + lane * 8, buf + (wave * 8 + j) * LAT_STRIDE);
     }
-    const int k = kt + rkey;
-    rope = u32x4{0u, 0u, 0u, 0u};
-    if (k < n && k < n_read) rope = gather16(a.kv, a.num_slots, a.stride, table[k], rcol, &ok);
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4*>(&ks[stage_key(kq, j) * KS_STRIDE + fb * 8]) = lat[j];
-    *reinterpret_cast<u32x4*>(&ks[rkey * KS_STRIDE + rcol * 8]) = rope;
-    // 8x8 transpose: column fb*8+c gets this quad's 8 keys in stage order.
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int d = c >> 1;
-      u32x4 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = lat[2 * e][d];
-        const uint32_t y = lat[2 * e + 1][d];
-        t[e] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-      }
-      *reinterpret_cast<u32x4*>(&vt[(fb * 8 + c) * VT_STRIDE + kq * 8]) = t;
-    }
+    const int kl = lane >> 3;              // key of this lane within the wave's 8
+    const int32_t sk = __shfl(vslot, kl);
+    const int key = wave * 8 + kl;         // key within the tile
+    const uint16_t* row = ((use >> kl) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
+    dma16(row + DV + rope_piece(key, lane & 7) * 8, buf + LAT_ELEMS + wave * 8 * DROPE);
   };
 
-  f32x4 o[O_BLOCKS];
-#pragma unroll
-  for (int c = 0; c < O_BLOCKS; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max of base-2 scores of this row
-  // Partial sums over this lane's keys (summed across the 4 lane groups at the
-  // end): l_run of the fp32 probabilities gives the lse; lb_run of the bf16
-  // probabilities that enter the value MFMA normalises the output, so the
-  // output is an exact weighted average of the value rows it was built from.
+  f32x16 o[O_HALF];
+  // The reference this row's probabilities are taken against, the largest
+  // tile max seen, and partial sums over this lane's keys (the other half of
+  // the row's keys is on lane ^ 32).  l sums the fp32 probabilities and gives
+  // the lse; lb sums the bf16 probabilities that enter the value MFMA and
+  // normalises the output, so the output is an exact weighted average of its
+  // value rows.  Both waves of a row half hold identical copies.
+  float m_ref = -INFINITY;
+  float m_seen = -INFINITY;
   float l_run = 0.f;
   float lb_run = 0.f;
 
-  if (k0 < k1) load_tile(k0);
-  for (int kt = k0; kt < k1; kt += TILE) {
-    __syncthreads();   // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (kt + TILE < k1) load_tile(kt + TILE);   // in flight during the math below
+  // per-lane LDS element offsets of the MFMA operands within a tile buffer
+  const int k_lat = lrow * LAT_STRIDE + lh * 8;   // K fragment, latent k-steps
+  int k_rope[4];                                  // K fragment, rope k-steps 32..35
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    k_rope[i] = LAT_ELEMS + lrow * DROPE + rope_piece(lrow, 2 * i + lh) * 8;
+  // value operand: block b = lane/16 of the wave reads keys 4*(b>>1) + i/4
+  // (+8) and columns 16*(b&1) + 4*(i%4) of each 32-column block (i = lane%16)
+  const int v_off = (4 * lh + ((lane & 15) >> 2)) * LAT_STRIDE + 16 * ((lane >> 4) & 1) +
+                    4 * (lane & 3) + hf * (O_HALF * 32);
 
-    // S^T = K . Q^T for the two 16-key blocks of the tile
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row) {
+    const int kt = k0 + t * TILE;
+    // partial S^T = K . Q^T over this wave's 288 score columns, in 3 groups
+    // of 6 k-steps.  The K fragments of group i+2 are requested from LDS
+    // before the MFMAs of group i (the fences keep the compiler from
+    // re-serialising reads and MFMAs, or from holding all 18 fragments).
+    constexpr int QG = 6;
+    f32x16 sacc;
 #pragma unroll
-    for (int k = 0; k < QK_STEPS; ++k) {
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+    bf16x8 kf[QK_HALF];
+    auto read_k = [&](int kk) {
+      const int k = hf * QK_HALF + kk;   // uniform
+      const int off = k < LAT_STEPS ? k_lat + k * 16 : k_rope[(k - LAT_STEPS) & 3];
+      kf[kk] = *reinterpret_cast<const bf16x8*>(buf + off);
+    };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&ks[(kb * 16 + lrow) * KS_STRIDE + k * 32 + lgrp * 8]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[k], sacc[kb], 0, 0, 0);
+    for (int kk = 0; kk < 2 * QG; ++kk) read_k(kk);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gi = 0; gi < QK_HALF / QG; ++gi) {
+      if (gi + 2 < QK_HALF / QG) {
+#pragma unroll
+        for (int kk = (gi + 2) * QG; kk < (gi + 3) * QG; ++kk) read_k(kk);
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int kk = gi * QG; kk < (gi + 1) * QG; ++kk)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // add the partner wave's partial scores
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+      xs[rh][hf][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const f32x4 v = xs[rh][hf ^ 1][qd][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc[4 * qd + e] += v[e];
     }
 
-    // mask + online softmax (base 2); lane holds 8 keys of row lrow
-    float sv[8];
+    // mask + softmax against the row's reference (base 2).  Register e of
+    // the lane holds key 8*(e/4) + 4*lh + e%4 of the tile for row lrow.
+    const bool need_mask = kt + TILE > L || kt + TILE > k1;   // uniform
+    float sv[16];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kp = kt + (j < 4 ? 4 * lgrp + j : 16 + 4 * lgrp + (j - 4));
-      bool vis = kp < n;
-      if (kp >= L) vis = vis && ((anc_row >> ((kp - L) & 63)) & 1ull);
-      sv[j] = vis ? sacc[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[j]);
+    for (int e = 0; e < 16; ++e) {
+      float x = sacc[e] * a.scale_log2;
+      if (need_mask) {
+        const int kp = kt + 8 * (e >> 2) + 4 * lh + (e & 3);
+        const int d = kp - L;
+        const bool in_tree = d < 0 || ((anc_row >> (d & 63)) & 1ull);
+        x = (kp < k1 && in_tree) ? x : -INFINITY;
+      }
+      sv[e] = x;
+      mx = fmaxf(mx, x);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    bf16x8 pf;
+    m_seen = fmaxf(m_seen, mx);
+    // a row with no reference yet (its sums are still 0) takes this tile's max
+    if (m_ref == -INFINITY) m_ref = mx;
+    if (mx > m_ref + REF_SLACK) restart_sh = 1u;   // all waves restart the pass
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    bf16x8 pf[2];
     float psum = 0.f;
     float pbsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = exp2f(sv[j] - m_use);
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sv[e] - m_use);
       const __bf16 pb = (__bf16)p;
-      pf[j] = pb;
+      pf[e >> 3][e & 7] = pb;
       psum += p;
       pbsum += (float)pb;
     }
-    l_run = l_run * alpha + psum;
-    lb_run = lb_run * alpha + pbsum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int c = 0; c < O_BLOCKS; ++c) o[c] *= alpha;
-    }
+    l_run += psum;
+    lb_run += pbsum;
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T over this wave's 256 output columns: 8 column blocks
+    // x 2 k-steps of 16 keys; V^T fragments by transpose reads, two column
+    // blocks ahead of their MFMAs.
+    bf16x8 vf[O_HALF][2];
+    auto read_v = [&](int cb) {
 #pragma unroll
-    for (int c = 0; c < O_BLOCKS; ++c) {
-      const bf16x8 vf =
-          *reinterpret_cast<const bf16x8*>(&vt[(c * 16 + lrow) * VT_STRIDE + lgrp * 8]);
-      o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[c], 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* p0 = buf + v_off + ks * 16 * LAT_STRIDE + cb * 32;
+        const i16x4 v0 = lds_read_tr16(p0);
+        const i16x4 v1 = lds_read_tr16(p0 + 8 * LAT_STRIDE);
+        const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        vf[cb][ks] = __builtin_bit_cast(bf16x8, v8);
+      }
+    };
+    constexpr int VG = 2;   // column blocks per group
+#pragma unroll
+    for (int cb = 0; cb < 2 * VG; ++cb) read_v(cb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gi = 0; gi < O_HALF / VG; ++gi) {
+      if (gi + 2 < O_HALF / VG) {
+#pragma unroll
+        for (int cb = (gi + 2) * VG; cb < (gi + 3) * VG; ++cb) read_v(cb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int cb = gi * VG; cb < (gi + 1) * VG; ++cb) {
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][0], pf[0], o[cb], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][1], pf[1], o[cb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // ---- pipeline.  Per wave, the vector-memory ops are issued in the order
+  // [slots(u+1), DMA(u)] for u = 0, 1, 2, ...; they complete in order, so
+  // once the DMA_PER_TILE copies of DMA(t+1) have been issued after DMA(t),
+  // "at most DMA_PER_TILE outstanding" means DMA(t) has landed in LDS (the
+  // slots of t+2, issued a whole tile earlier, are waited for with it).
+  // Buffer t % 3 holds tile t; DMA(t+2) is issued after the barrier that
+  // ends every wave's use of tile t-1, the buffer's previous content.
+  uint64_t anc_row = 0ull;
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int c = 0; c < O_HALF; ++c) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[c][e] = 0.f;
+    }
+    l_run = 0.f;
+    lb_run = 0.f;
+    if (tid == 0) restart_sh = 0u;
+    int32_t slot_next = 0;
+    if (ntiles > 0) {
+      const int32_t s0 = load_slot(0);
+      slot_next = load_slot(ntiles > 1 ? 1 : 0);
+      issue_tile(0, s0, tiles);
+      if (ntiles > 1) {
+        const int32_t s1 = slot_next;
+        slot_next = load_slot(ntiles > 2 ? 2 : 1);
+        issue_tile(1, s1, tiles + BUF_ELEMS);
+      }
+    }
+    __syncthreads();   // anc[], status_sh and restart_sh ready
+    if (pass == 0) anc_row = row_ok ? anc[rho / H] : 0ull;
+
+    int cur_buf = 0;   // tile t lives in buffer t % 3
+    bool restart = false;
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 1 < ntiles) {
+        wait_vmcnt<DMA_PER_TILE>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();   // tile t is in LDS; every wave is done with tile t-1
+      if (restart_sh != 0u && pass + 1 < MAX_PASSES) {   // uniform: read after the barrier
+        restart = true;
+        break;
+      }
+      if (t + 2 < ntiles) {
+        const int32_t sl = slot_next;
+        slot_next = load_slot(t + 3 < ntiles ? t + 3 : t + 2);
+        const int later = cur_buf == 0 ? 2 : cur_buf - 1;   // (t + 2) % 3
+        issue_tile(t + 2, sl, tiles + later * BUF_ELEMS);
+      }
+      compute(t, tiles + cur_buf * BUF_ELEMS, anc_row);
+      wait_lgkmcnt0();
+      cur_buf = cur_buf == 2 ? 0 : cur_buf + 1;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();   // all copies landed and all waves are done with the tiles
+    if (!restart) restart = restart_sh != 0u && pass + 1 < MAX_PASSES;
+    if (!restart) break;
+    m_ref = m_seen;
   }
 
-  // ---- epilogue: normalise and store this work item's partial
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  float lb_tot = lb_run + __shfl_xor(lb_run, 16);
-  lb_tot += __shfl_xor(lb_tot, 32);
-  const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
-  const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-  if (row_ok) {
-    const int64_t prow = (int64_t)w * ROWS + wave * 16 + lrow;
-    float* po = a.part_o + prow * DV + lgrp * 4;
+  // ---- store this work item's partial in the MFMA output layout: entry
+  // ((rh * 2 + hf) * O_HALF + cb) * 4 + qd, lane holds float4 qd of lane's
+  // register block cb, i.e. row rh*32 + lane%32 and columns
+  // 256*hf + 32*cb + 8*qd + 4*(lane/32) .. +3 (rows past T*H are never read).
+  {
+    const float l = l_run + __shfl_xor(l_run, 32);
+    const float lb = lb_run + __shfl_xor(lb_run, 32);
+    f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (int64_t)w * PART_VEC +
+                (rh * 2 + hf) * (O_HALF * 4 * 64) + lane;
 #pragma unroll
-    for (int c = 0; c < O_BLOCKS; ++c) *reinterpret_cast<f32x4*>(po + c * 16) = o[c] * inv;
-    if (lgrp == 0) a.part_lse[prow] = lse2;
+    for (int cb = 0; cb < O_HALF; ++cb) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        po[(cb * 4 + qd) * 64] = f32x4{o[cb][4 * qd], o[cb][4 * qd + 1], o[cb][4 * qd + 2], o[cb][4 * qd + 3]};
+    }
+    if (hf == 0 && lh == 0) {
+      const float lse2 = l > 0.f ? m_ref + log2f(l) : -INFINITY;
+      *reinterpret_cast<float2*>(a.part_lse + ((int64_t)w * ROWS + rh * 32 + lrow) * 2) =
+          make_float2(lse2, lb);
+    }
   }
-  if (!ok) st |= VA_STATUS_BAD_SLOT;
+  st |= bad;
   if (st) atomicOr(&status_sh, st);
   __syncthreads();
   if (tid == 0) a.status[w] = status_sh;
 }
 
-// One block per query row: merge the row's splits by log-sum-exp.
-__global__ __launch_bounds__(128) void va_reduce_kernel(ReduceArgs a) {
-  const int row = blockIdx.x;   // global (node, head) row
-  const int tid = threadIdx.x;  // 4 output columns each
-  const int H = a.num_heads;
-  int r = 0;
-  while (r + 1 < a.num_requests && a.tree_begin[r + 1] * H <= row) ++r;
-  const int rho = row - a.tree_begin[r] * H;
-  const int g = rho / ROWS;
-  const int ri = rho - g * ROWS;
-  const int ns = a.nsplit[r];
-  const int64_t wb = (int64_t)a.work_begin[r] + (int64_t)g * ns;
+// Log-sum-exp merge of the splits.  One block of 256 threads per (request,
+// row group, row half, output-column half, 32-column block, float4 quad):
+// 32 rows x 8 columns, read as one contiguous 1 KB piece per split.  The
+// threads first turn each split's (lse, weight sum) into the coefficient
+// exp2(lse_s - max) / lb_s of every row; then the 4 waves each accumulate a
+// quarter of the splits and add up through LDS.
+constexpr int RED_THREADS = 256;
+constexpr int RED_PIECES = 2 * 2 * O_HALF * 4;   // blocks per row group
 
-  uint32_t st = 0u;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) {
-    st |= a.status[wb + s];
-    M = fmaxf(M, a.part_lse[(wb + s) * ROWS + ri]);
+__global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
+  __shared__ float coef[VA_MAX_SPLITS][32];
+  __shared__ float red_m[8][32];
+  __shared__ float red_w[8][32];
+  __shared__ uint32_t red_s[8][32];
+  __shared__ f32x4 part[4][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int b = blockIdx.x;
+  int r = 0;
+  // block ranges: request r owns num_groups[r] * RED_PIECES blocks
+  while (r + 1 < a.num_requests && b >= a.num_groups[r] * RED_PIECES) {
+    b -= a.num_groups[r] * RED_PIECES;
+    ++r;
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int g = b / RED_PIECES;
+  const int piece = b - g * RED_PIECES;    // ((rh * 2 + hf) * O_HALF + cb) * 4 + qd
+  const int rh = piece / (2 * O_HALF * 4);
+  const int hf = (piece / (O_HALF * 4)) & 1;
+  const int cb = (piece >> 2) % O_HALF;
+  const int qd = piece & 3;
+  const int ns = a.nsplit[r];
+  const int G = a.num_groups[r];
+  const int H = a.num_heads;
+  const int rows_r = (a.tree_begin[r + 1] - a.tree_begin[r]) * H;
+  const int64_t wbase = (int64_t)a.work_begin[r] + g;   // work item of split s: wbase + s * G
+
+  // per-row max and weight sums over the splits: thread = (split group sg, row)
+  const int row = tid & 31;
+  const int sg = tid >> 5;
+  float m = -INFINITY;
+  uint32_t st = 0u;
+  for (int s = sg; s < ns; s += 8) {
+    const int64_t w = wbase + (int64_t)s * G;
+    m = fmaxf(m, a.part_lse[(w * ROWS + rh * 32 + row) * 2]);
+    st |= a.status[w];
+  }
+  red_m[sg][row] = m;
+  red_s[sg][row] = st;
+  __syncthreads();
+  float M = red_m[0][row];
+  uint32_t S = red_s[0][row];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    M = fmaxf(M, red_m[i][row]);
+    S |= red_s[i][row];
+  }
   float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const float ls = a.part_lse[(wb + s) * ROWS + ri];
-      if (ls == -INFINITY) continue;
-      const float wt = exp2f(ls - M);
-      wsum += wt;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + ((wb + s) * ROWS + ri) * DV + tid * 4);
-      acc += wt * v;
+  for (int s = sg; s < ns; s += 8) {
+    const int64_t w = wbase + (int64_t)s * G;
+    const float2 v = *reinterpret_cast<const float2*>(a.part_lse + (w * ROWS + rh * 32 + row) * 2);
+    const float e = (v.x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(v.x - M);
+    wsum += e;
+    coef[s][row] = (e > 0.f && v.y > 0.f) ? e / v.y : 0.f;
+  }
+  red_w[sg][row] = wsum;
+  __syncthreads();
+
+  // weighted sum of this block's 1 KB piece over the splits
+  const int prow = lane & 31;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o) + piece * 64 + lane;
+  for (int s = wave; s < ns; s += 4) {
+    const float c = coef[s][prow];
+    if (c != 0.f) acc += c * src[(wbase + (int64_t)s * G) * PART_VEC];
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (tid < 64) {
+    const f32x4 tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    float W = 0.f;
+    uint32_t Sr = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      W += red_w[i][prow];
+      Sr |= red_s[i][prow];
+    }
+    float Mr = red_m[0][prow];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) Mr = fmaxf(Mr, red_m[i][prow]);
+    const int rr = g * ROWS + rh * 32 + prow;   // row within the request
+    if (rr < rows_r) {
+      float res[4];
+      float lse_out;
+      if (Sr != 0u) {
+        res[0] = res[1] = res[2] = res[3] = NAN;
+        lse_out = NAN;
+      } else if (W > 0.f) {
+        const float inv = 1.f / W;
+        res[0] = tot[0] * inv; res[1] = tot[1] * inv; res[2] = tot[2] * inv; res[3] = tot[3] * inv;
+        lse_out = (Mr + log2f(W)) * LN2;
+      } else {
+        res[0] = res[1] = res[2] = res[3] = 0.f;
+        lse_out = -INFINITY;
+      }
+      const int64_t orow = (int64_t)a.tree_begin[r] * H + rr;
+      const int col = hf * (O_HALF * 32) + cb * 32 + 8 * qd + 4 * (lane >> 5);
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[0]) | ((uint32_t)f32_to_bf16_rne(res[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[2]) | ((uint32_t)f32_to_bf16_rne(res[3]) << 16);
+      *reinterpret_cast<uint2*>(a.out + orow * DV + col) = make_uint2(lo, hi);
+      if (piece == 0 && lane < 32) a.lse[orow] = lse_out;
+      if (piece == 2 * O_HALF * 4 && lane < 32) a.lse[orow] = lse_out;   // rows of row half 1
     }
   }
-  float res[4];
-  float lse_out;
-  if (st != 0u) {
-    res[0] = res[1] = res[2] = res[3] = NAN;
-    lse_out = NAN;
-  } else if (wsum > 0.f) {
-    const float inv = 1.f / wsum;
-    res[0] = acc[0] * inv; res[1] = acc[1] * inv; res[2] = acc[2] * inv; res[3] = acc[3] * inv;
-    lse_out = (M + log2f(wsum)) * LN2;
-  } else {
-    res[0] = res[1] = res[2] = res[3] = 0.f;
-    lse_out = -INFINITY;
-  }
-  uint32_t lo = (uint32_t)f32_to_bf16_rne(res[0]) | ((uint32_t)f32_to_bf16_rne(res[1]) << 16);
-  uint32_t hi = (uint32_t)f32_to_bf16_rne(res[2]) | ((uint32_t)f32_to_bf16_rne(res[3]) << 16);
-  *reinterpret_cast<uint2*>(a.out + (int64_t)row * DV + tid * 4) = make_uint2(lo, hi);
-  if (tid == 0) a.lse[row] = lse_out;
+  (void)S;
 }
 
-// Diagnostic: pool rows through the partial pass's 16-byte gather.
-__global__ __launch_bounds__(256) void va_gather_kernel(const uint16_t* kv, int64_t num_slots,
-                                                        int32_t stride, const int32_t* table,
-                                                        int32_t n, uint16_t* dst) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)n * (DQK / 8)) return;
-  const int k = (int)(i / (DQK / 8));
-  const int c8 = (int)(i - (int64_t)k * (DQK / 8));
-  bool ok = true;
-  u32x4 v = gather16(kv, num_slots, stride, table[k], c8, &ok);
-  if (!ok) v = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-  *reinterpret_cast<u32x4*>(dst + (int64_t)k * DQK + c8 * 8) = v;
+// Diagnostic: pool rows through the partial pass's table/slot checks and its
+// 16-byte global->LDS copy; one block of 64 threads per row.
+__global__ __launch_bounds__(64) void va_gather_kernel(const uint16_t* kv, int64_t num_slots,
+                                                       int32_t stride, const int32_t* table,
+                                                       int32_t n, uint16_t* dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t row_lds[LAT_STRIDE + DROPE];
+  const int k = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t slot = table_entry(table, k, n);
+  const bool inside = slot >= 0 && (int64_t)slot < num_slots;
+  const uint16_t* row = inside ? kv + (int64_t)slot * stride : va_zero_row;
+  dma16(row + lane * 8, row_lds);
+  if (lane < 8) {
+    // same rope path as the partial pass, for key index 0 of a tile
+    dma16(row + DV + rope_piece(0, lane) * 8, row_lds + LAT_STRIDE);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int i = lane; i < DQK / 8; i += 64) {
+    u32x4 v;
+    if (i < DV / 8) {
+      v = *reinterpret_cast<const u32x4*>(row_lds + i * 8);
+    } else {
+      const int piece = i - DV / 8;
+      v = *reinterpret_cast<const u32x4*>(row_lds + LAT_STRIDE + rope_piece(0, piece) * 8);
+    }
+    if (!inside) v = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+    *reinterpret_cast<u32x4*>(dst + (int64_t)k * DQK + i * 8) = v;
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -494,7 +759,7 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
   p.total_tree = (int32_t)tree;
   p.total_rows = (int32_t)(tree * num_heads);
   const int64_t o_bytes = align256(work * ROWS * DV * (int64_t)sizeof(float));
-  const int64_t lse_bytes = align256(work * ROWS * (int64_t)sizeof(float));
+  const int64_t lse_bytes = align256(work * ROWS * 2 * (int64_t)sizeof(float));
   const int64_t st_bytes = align256(work * (int64_t)sizeof(uint32_t));
   p.lse_offset = o_bytes;
   p.status_offset = o_bytes + lse_bytes;
@@ -529,6 +794,7 @@ int verify_attn_run(const va_plan* plan, const uint16_t* q, const uint16_t* kv_p
   a.stride = kv_row_stride;
   a.num_requests = plan->num_requests;
   a.num_heads = plan->num_heads;
+  a.total_work = plan->total_work;
   a.scale_log2 = sm_scale * LOG2E;
   a.slot_table = slot_table;
   a.slot_table_len = slot_table_len;
@@ -543,12 +809,14 @@ int verify_attn_run(const va_plan* plan, const uint16_t* q, const uint16_t* kv_p
     a.num_tree[r] = plan->num_tree[r];
     a.max_prefix[r] = plan->max_prefix[r];
     a.nsplit[r] = plan->nsplit[r];
+    a.num_groups[r] = plan->num_groups[r];
   }
   for (int r = 0; r <= plan->num_requests; ++r) {
     a.tree_begin[r] = plan->tree_begin[r];
     a.work_begin[r] = plan->work_begin[r];
   }
-  hipLaunchKernelGGL(va_partial_kernel, dim3(plan->total_work), dim3(THREADS), 0,
+  const unsigned grid = 8u * (unsigned)((plan->total_work + 7) / 8);   // see the XCD work order
+  hipLaunchKernelGGL(va_partial_kernel, dim3(grid), dim3(THREADS), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
@@ -569,12 +837,17 @@ int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out
   a.lse = lse;
   a.num_requests = plan->num_requests;
   a.num_heads = plan->num_heads;
-  for (int r = 0; r < plan->num_requests; ++r) a.nsplit[r] = plan->nsplit[r];
+  for (int r = 0; r < plan->num_requests; ++r) {
+    a.nsplit[r] = plan->nsplit[r];
+    a.num_groups[r] = plan->num_groups[r];
+  }
   for (int r = 0; r <= plan->num_requests; ++r) {
     a.tree_begin[r] = plan->tree_begin[r];
     a.work_begin[r] = plan->work_begin[r];
   }
-  hipLaunchKernelGGL(va_reduce_kernel, dim3(plan->total_rows), dim3(DV / 4), 0,
+  int blocks = 0;
+  for (int r = 0; r < plan->num_requests; ++r) blocks += plan->num_groups[r] * RED_PIECES;
+  hipLaunchKernelGGL(va_reduce_kernel, dim3(blocks), dim3(RED_THREADS), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
@@ -616,9 +889,7 @@ int verify_attn_gather_rows(const uint16_t* kv_pool, int64_t num_slots, int32_t 
   if (n < 0 || num_slots < 1 || kv_row_stride < DQK) return VA_ERR_SHAPE;
   if (!aligned16(kv_pool) || !aligned16(dst) || (kv_row_stride % 8) != 0) return VA_ERR_ALIGN;
   if (n == 0) return VA_OK;
-  const int64_t pieces = (int64_t)n * (DQK / 8);
-  const int64_t blocks = (pieces + 255) / 256;
-  hipLaunchKernelGGL(va_gather_kernel, dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL(va_gather_kernel, dim3((unsigned)n), dim3(64), 0,
                      static_cast<hipStream_t>(stream), kv_pool, num_slots, kv_row_stride,
                      slot_table, n, dst);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;

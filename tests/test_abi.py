@@ -59,8 +59,8 @@ def test_plan_long_prefix_h8_t16():
     assert p.total_tree == 16 and p.total_rows == 128
     o = 256 * 64 * 512 * 4
     assert p.lse_offset == o
-    assert p.status_offset == o + 256 * 64 * 4
-    assert p.workspace_bytes == o + 256 * 64 * 4 + 1024
+    assert p.status_offset == o + 256 * 64 * 8
+    assert p.workspace_bytes == o + 256 * 64 * 8 + 1024
 
 
 def test_plan_full_heads_and_ragged_batch():
