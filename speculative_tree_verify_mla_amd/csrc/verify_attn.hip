@@ -62,17 +62,16 @@ constexpr int DQK = VA_D_QK;      // 576
 constexpr int DV = VA_D_V;        // 512: value columns = latent columns
 constexpr int DROPE = DQK - DV;   // 64 rope columns
 constexpr int TILE = 32;          // keys per LDS tile
-constexpr int THREADS = 256;      // 4 waves
+constexpr int THREADS = 512;      // 8 waves, 2 per SIMD
 constexpr int ROWS = 64;          // query rows per work item
 constexpr int LAT_STRIDE = DV + 24;               // bf16 per latent row in LDS (1072 B)
 constexpr int LAT_ELEMS = TILE * LAT_STRIDE;
 constexpr int BUF_ELEMS = LAT_ELEMS + TILE * DROPE;  // one tile buffer: 38,400 B
 constexpr int QK_STEPS = DQK / 16;   // 36 MFMA k-steps (16 columns each) for the score
-constexpr int QK_HALF = QK_STEPS / 2; // 18 of them per wave
+constexpr int QK_Q = QK_STEPS / 4;    // 9 of them per wave (a quarter of the columns)
 constexpr int LAT_STEPS = DV / 16;   // the first 32 are latent columns, the last 4 rope
-constexpr int O_HALF = DV / 32 / 2;  // 8 MFMA column blocks (32 columns) of the output per wave
+constexpr int O_Q = DV / 32 / 4;     // 4 MFMA column blocks (32 columns) of the output per wave
 constexpr int PART_VEC = ROWS * DV / 4;  // float4 entries of one work item's partial output
-constexpr int DMA_PER_TILE = TILE / 4 + 1;  // per wave: 8 latent rows + 1 block of 8 rope rows
 constexpr int MIN_KEYS_PER_SPLIT = 256;
 constexpr float REF_SLACK = 64.f;  // log2 units: probabilities stay <= 2^64
 constexpr int MAX_PASSES = 8;      // restarts of a work item with a raised reference
@@ -83,6 +82,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -180,7 +180,10 @@ __device__ __forceinline__ int rope_piece(int key, int piece) { return piece ^ (
 
 __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[3 * BUF_ELEMS];
-  __shared__ f32x4 xs[2][2][4][64];   // partial scores [row half][half][register quad][lane]
+  __shared__ f32x4 xs[2][4][4][64];     // partial scores [row half][quarter][register quad][lane]
+  __shared__ u32x2 xp[2][4][64];        // bf16 probabilities [row half][register quad][lane]
+  __shared__ float xm[2][4][32];        // per-row values exchanged between the 4 quarter waves
+  __shared__ float xl[2][4][2][32];     // per-row sums l, lb of each quarter wave
   __shared__ uint64_t anc[VA_MAX_TREE];
   __shared__ uint32_t status_sh;
   __shared__ uint32_t restart_sh;
@@ -189,9 +192,9 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = wave & 1;      // row half of the work item's 64 rows
-  const int hf = wave >> 1;     // score-column half and output-column half
+  const int qq = wave >> 1;     // quarter: score columns, register quad (keys), output columns
   const int lrow = lane & 31;   // MFMA column: this lane's query row within the row half
-  const int lh = lane >> 5;     // MFMA k-half of this lane (keys 4*lh + 8*j + i of a tile)
+  const int lh = lane >> 5;     // MFMA k-half of this lane
 
   // Work items are ordered (request, split, row group); block b runs on XCD
   // b % 8, so each XCD takes a contiguous run of work items and the row
@@ -253,154 +256,164 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     anc[tid] = m;
   }
 
-  // ---- Q fragments of this lane's row over this wave's 288 score columns
+  // ---- Q fragments of this lane's row over this wave's 144 score columns
   const int rho = g * ROWS + rh * 32 + lrow;
   const bool row_ok = rho < rows_r;
-  bf16x8 qf[QK_HALF];
+  bf16x8 qf[QK_Q];
   {
     const int64_t qrow = (int64_t)a.tree_begin[r] * H + (row_ok ? rho : 0);
-    const uint16_t* qp = a.q + qrow * DQK + hf * (QK_HALF * 16) + lh * 8;
+    const uint16_t* qp = a.q + qrow * DQK + qq * (QK_Q * 16) + lh * 8;
 #pragma unroll
-    for (int k = 0; k < QK_HALF; ++k) {
+    for (int k = 0; k < QK_Q; ++k) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qp + k * 16);
       if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
       qf[k] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  // ---- tile loader: this wave moves keys 8*wave .. +7 of a tile: 8 latent
-  // rows (one 1 KB DMA each) and their rope parts (one DMA of 8 x 128 B).
+  // ---- tile loader.  Lane l holds the slot of key l % 32 of the tile.
+  // Wave w copies the latent rows of keys 4w .. 4w+3 (one 1 KB DMA each);
+  // waves 0..3 also copy the rope parts of keys 8w .. 8w+7 (one DMA).
   uint32_t bad = 0u;
+  const bool rope_wave = wave < 4;
   auto load_slot = [&](int t) -> int32_t {
-    return table_entry(table, k0 + t * TILE + wave * 8 + (lane & 7), k1);
+    return table_entry(table, k0 + t * TILE + (lane & 31), k1);
   };
   auto issue_tile = [&](int t, int32_t vslot, uint16_t* buf) {
-    const int k = k0 + t * TILE + wave * 8 + (lane & 7);
+    const int k = k0 + t * TILE + (lane & 31);
     const bool exists = k < k1;
     const bool inside = vslot >= 0 && (int64_t)vslot < a.num_slots;
     if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
-    const uint64_t use = __ballot(exists && inside);   // bit j: key 8*wave + j is read
+    const uint64_t use = __ballot(exists && inside);   // bit j: key j of the tile is read
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int32_t sj = __builtin_amdgcn_readlane(vslot, j);
-      const uint16_t* row = ((use >> j) & 1ull) ? a.kv + (int64_t)sj * a.stride : va_zero_row;
-      dma16(row + lane * 8, buf + (wave * 8 + j) * LAT_STRIDE);
+    for (int j = 0; j < 4; ++j) {
+      const int key = wave * 4 + j;
+      const int32_t sj = __builtin_amdgcn_readlane(vslot, key);
+      const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sj * a.stride : va_zero_row;
+      dma16(row + lane * 8, buf + key * LAT_STRIDE);
     }
-    const int kl = lane >> 3;              // key of this lane within the wave's 8
-    const int32_t sk = __shfl(vslot, kl);
-    const int key = wave * 8 + kl;         // key within the tile
-    const uint16_t* row = ((use >> kl) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
-    dma16(row + DV + rope_piece(key, lane & 7) * 8, buf + LAT_ELEMS + wave * 8 * DROPE);
+    if (rope_wave) {
+      const int key = wave * 8 + (lane >> 3);   // key of this lane within the tile
+      const int32_t sk = __shfl(vslot, key);
+      const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
+      dma16(row + DV + rope_piece(key, lane & 7) * 8, buf + LAT_ELEMS + wave * 8 * DROPE);
+    }
   };
 
-  f32x16 o[O_HALF];
-  // The reference this row's probabilities are taken against, the largest
-  // tile max seen, and partial sums over this lane's keys (the other half of
-  // the row's keys is on lane ^ 32).  l sums the fp32 probabilities and gives
-  // the lse; lb sums the bf16 probabilities that enter the value MFMA and
-  // normalises the output, so the output is an exact weighted average of its
-  // value rows.  Both waves of a row half hold identical copies.
+  f32x16 o[O_Q];
+  // The reference this row's probabilities are taken against (common to the
+  // 4 quarter waves), the largest tile max this wave has seen, and partial
+  // sums over this wave's keys (the other half of the quad's keys is on lane
+  // ^ 32).  l sums the fp32 probabilities and gives the lse; lb sums the bf16
+  // probabilities that enter the value MFMA and normalises the output, so the
+  // output is an exact weighted average of its value rows.
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;
   float l_run = 0.f;
   float lb_run = 0.f;
 
   // per-lane LDS element offsets of the MFMA operands within a tile buffer
-  const int k_lat = lrow * LAT_STRIDE + lh * 8;   // K fragment, latent k-steps
-  int k_rope[4];                                  // K fragment, rope k-steps 32..35
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    k_rope[i] = LAT_ELEMS + lrow * DROPE + rope_piece(lrow, 2 * i + lh) * 8;
+  const int k_lat = lrow * LAT_STRIDE + lh * 8;        // K fragment, latent k-steps
+  const int k_rope = LAT_ELEMS + lrow * DROPE;          // K fragment row, rope k-steps 32..35
   // value operand: block b = lane/16 of the wave reads keys 4*(b>>1) + i/4
   // (+8) and columns 16*(b&1) + 4*(i%4) of each 32-column block (i = lane%16)
   const int v_off = (4 * lh + ((lane & 15) >> 2)) * LAT_STRIDE + 16 * ((lane >> 4) & 1) +
-                    4 * (lane & 3) + hf * (O_HALF * 32);
+                    4 * (lane & 3) + qq * (O_Q * 32);
+  // this wave's register quad: keys 8*qq + 4*lh + i of the tile
+  const int qkey = 8 * qq + 4 * lh;
 
-  auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row) {
+  // Consumes tile t (one buffer).  `first` is set on the first tile of a
+  // pass: the quarter waves then agree on each row's reference.
+  auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row, bool first) {
     const int kt = k0 + t * TILE;
-    // partial S^T = K . Q^T over this wave's 288 score columns, in 3 groups
-    // of 6 k-steps.  The K fragments of group i+2 are requested from LDS
-    // before the MFMAs of group i (the fences keep the compiler from
-    // re-serialising reads and MFMAs, or from holding all 18 fragments).
-    constexpr int QG = 6;
+    // partial S^T = K . Q^T over this wave's 144 score columns
     f32x16 sacc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-    bf16x8 kf[QK_HALF];
-    auto read_k = [&](int kk) {
-      const int k = hf * QK_HALF + kk;   // uniform
-      const int off = k < LAT_STEPS ? k_lat + k * 16 : k_rope[(k - LAT_STEPS) & 3];
-      kf[kk] = *reinterpret_cast<const bf16x8*>(buf + off);
-    };
+    bf16x8 kf[QK_Q];
 #pragma unroll
-    for (int kk = 0; kk < 2 * QG; ++kk) read_k(kk);
+    for (int kk = 0; kk < QK_Q; ++kk) {
+      const int k = qq * QK_Q + kk;   // uniform
+      const int off = k < LAT_STEPS ? k_lat + k * 16
+                                    : k_rope + rope_piece(lrow, 2 * (k - LAT_STEPS) + lh) * 8;
+      kf[kk] = *reinterpret_cast<const bf16x8*>(buf + off);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int gi = 0; gi < QK_HALF / QG; ++gi) {
-      if (gi + 2 < QK_HALF / QG) {
-#pragma unroll
-        for (int kk = (gi + 2) * QG; kk < (gi + 3) * QG; ++kk) read_k(kk);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int kk = gi * QG; kk < (gi + 1) * QG; ++kk)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sacc, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // add the partner wave's partial scores
+    for (int kk = 0; kk < QK_Q; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sacc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // hand each register quad to the wave that owns it; add the 3 others' partials
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
-      xs[rh][hf][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
+      xs[rh][qq][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
+    wait_lgkmcnt0();   // the LDS writes are done before other waves pass the barrier
     __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const f32x4 v = xs[rh][hf ^ 1][qd][lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[4 * qd + e] += v[e];
-    }
+    // (the own partial is read back too: indexing sacc by the wave's quarter
+    // would need register-indexed moves)
+    const f32x4 sq0 = xs[rh][0][qq][lane];
+    const f32x4 sq1 = xs[rh][1][qq][lane];
+    const f32x4 sq2 = xs[rh][2][qq][lane];
+    const f32x4 sq3 = xs[rh][3][qq][lane];
+    f32x4 sq = (sq0 + sq1) + (sq2 + sq3);
 
-    // mask + softmax against the row's reference (base 2).  Register e of
-    // the lane holds key 8*(e/4) + 4*lh + e%4 of the tile for row lrow.
-    const bool need_mask = kt + TILE > L || kt + TILE > k1;   // uniform
-    float sv[16];
-    float mx = -INFINITY;
+    // mask (only on tiles reaching past the prefix or the split end)
+    if (kt + TILE > L || kt + TILE > k1) {   // uniform
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float x = sacc[e] * a.scale_log2;
-      if (need_mask) {
-        const int kp = kt + 8 * (e >> 2) + 4 * lh + (e & 3);
+      for (int i = 0; i < 4; ++i) {
+        const int kp = kt + qkey + i;
         const int d = kp - L;
         const bool in_tree = d < 0 || ((anc_row >> (d & 63)) & 1ull);
-        x = (kp < k1 && in_tree) ? x : -INFINITY;
+        sq[i] = (kp < k1 && in_tree) ? sq[i] : -INFINITY;
       }
-      sv[e] = x;
-      mx = fmaxf(mx, x);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mx = fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));   // this wave's keys of the row
+    mx *= a.scale_log2;
     m_seen = fmaxf(m_seen, mx);
-    // a row with no reference yet (its sums are still 0) takes this tile's max
-    if (m_ref == -INFINITY) m_ref = mx;
-    if (mx > m_ref + REF_SLACK) restart_sh = 1u;   // all waves restart the pass
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    bf16x8 pf[2];
-    float psum = 0.f;
-    float pbsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sv[e] - m_use);
-      const __bf16 pb = (__bf16)p;
-      pf[e >> 3][e & 7] = pb;
-      psum += p;
-      pbsum += (float)pb;
+    if (first) {
+      // reference = the row's max over the whole tile (all 4 quads)
+      if (lh == 0) xm[rh][qq][lrow] = mx;
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      const float r4 = fmaxf(fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]),
+                             fmaxf(xm[rh][2][lrow], xm[rh][3][lrow]));
+      if (m_ref == -INFINITY) m_ref = r4;
+    } else if (mx > m_ref + REF_SLACK) {
+      restart_sh = 1u;   // all waves restart the pass with a raised reference
     }
-    l_run += psum;
-    lb_run += pbsum;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    // probabilities of the quad's 4 keys: exp2(s * scale - m)
+    float p[4];
+    __bf16 pb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[i], a.scale_log2, -m_use));
+      pb[i] = (__bf16)p[i];
+    }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p01 = {pb[0], pb[1]};
+    const bf16x2 p23 = {pb[2], pb[3]};
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    lb_run = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, __builtin_amdgcn_fdot2_f32_bf16(p01, ones, lb_run, false), false);
+    xp[rh][qq][lane] = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    // B operand of k-step ks: the probabilities of quads 2ks and 2ks+1
+    bf16x8 pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x2 lo = xp[rh][2 * ks][lane];
+      const u32x2 hi = xp[rh][2 * ks + 1][lane];
+      pf[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
 
-    // O^T += V^T . P^T over this wave's 256 output columns: 8 column blocks
-    // x 2 k-steps of 16 keys; V^T fragments by transpose reads, two column
-    // blocks ahead of their MFMAs.
-    bf16x8 vf[O_HALF][2];
-    auto read_v = [&](int cb) {
+    // O^T += V^T . P^T over this wave's 128 output columns: 4 column blocks
+    // x 2 k-steps of 16 keys; V^T fragments by transpose reads
+    bf16x8 vf[O_Q][2];
+#pragma unroll
+    for (int cb = 0; cb < O_Q; ++cb) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const uint16_t* p0 = buf + v_off + ks * 16 * LAT_STRIDE + cb * 32;
@@ -409,38 +422,27 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
         const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         vf[cb][ks] = __builtin_bit_cast(bf16x8, v8);
       }
-    };
-    constexpr int VG = 2;   // column blocks per group
-#pragma unroll
-    for (int cb = 0; cb < 2 * VG; ++cb) read_v(cb);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int gi = 0; gi < O_HALF / VG; ++gi) {
-      if (gi + 2 < O_HALF / VG) {
-#pragma unroll
-        for (int cb = (gi + 2) * VG; cb < (gi + 3) * VG; ++cb) read_v(cb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int cb = gi * VG; cb < (gi + 1) * VG; ++cb) {
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][0], pf[0], o[cb], 0, 0, 0);
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][1], pf[1], o[cb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int cb = 0; cb < O_Q; ++cb) {
+      o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][0], pf[0], o[cb], 0, 0, 0);
+      o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][1], pf[1], o[cb], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- pipeline.  Per wave, the vector-memory ops are issued in the order
   // [slots(u+1), DMA(u)] for u = 0, 1, 2, ...; they complete in order, so
-  // once the DMA_PER_TILE copies of DMA(t+1) have been issued after DMA(t),
-  // "at most DMA_PER_TILE outstanding" means DMA(t) has landed in LDS (the
-  // slots of t+2, issued a whole tile earlier, are waited for with it).
-  // Buffer t % 3 holds tile t; DMA(t+2) is issued after the barrier that
-  // ends every wave's use of tile t-1, the buffer's previous content.
+  // once the copies of DMA(t+1) have been issued after DMA(t), "at most that
+  // many outstanding" means DMA(t) has landed in LDS (the slots of t+2,
+  // issued a whole tile earlier, are waited for with it).  Buffer t % 3
+  // holds tile t; DMA(t+2) is issued after the barrier that ends every
+  // wave's use of tile t-1, the buffer's previous content.
   uint64_t anc_row = 0ull;
   for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int c = 0; c < O_HALF; ++c) {
+    for (int c = 0; c < O_Q; ++c) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[c][e] = 0.f;
     }
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     bool restart = false;
     for (int t = 0; t < ntiles; ++t) {
       if (t + 1 < ntiles) {
-        wait_vmcnt<DMA_PER_TILE>();
+        if (rope_wave) wait_vmcnt<5>(); else wait_vmcnt<4>();   // this wave's copies per tile
       } else {
         wait_vmcnt<0>();
       }
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
         const int later = cur_buf == 0 ? 2 : cur_buf - 1;   // (t + 2) % 3
         issue_tile(t + 2, sl, tiles + later * BUF_ELEMS);
       }
-      compute(t, tiles + cur_buf * BUF_ELEMS, anc_row);
+      compute(t, tiles + cur_buf * BUF_ELEMS, anc_row, t == 0);
       wait_lgkmcnt0();
       cur_buf = cur_buf == 2 ? 0 : cur_buf + 1;
     }
@@ -488,28 +490,39 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     __syncthreads();   // all copies landed and all waves are done with the tiles
     if (!restart) restart = restart_sh != 0u && pass + 1 < MAX_PASSES;
     if (!restart) break;
-    m_ref = m_seen;
+    // raise the reference to the largest tile max any quarter wave has seen
+    if (lh == 0) xm[rh][qq][lrow] = m_seen;
+    __syncthreads();
+    m_ref = fmaxf(fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]), fmaxf(xm[rh][2][lrow], xm[rh][3][lrow]));
+    __syncthreads();
   }
 
   // ---- store this work item's partial in the MFMA output layout: entry
-  // ((rh * 2 + hf) * O_HALF + cb) * 4 + qd, lane holds float4 qd of lane's
-  // register block cb, i.e. row rh*32 + lane%32 and columns
-  // 256*hf + 32*cb + 8*qd + 4*(lane/32) .. +3 (rows past T*H are never read).
+  // ((rh * 4 + qq) * O_Q + cb) * 4 + qd, lane holds float4 qd of the lane's
+  // register block cb: row rh*32 + lane%32, columns
+  // 128*qq + 32*cb + 8*qd + 4*(lane/32) .. +3 (rows past T*H are never read).
   {
-    const float l = l_run + __shfl_xor(l_run, 32);
-    const float lb = lb_run + __shfl_xor(lb_run, 32);
     f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (int64_t)w * PART_VEC +
-                (rh * 2 + hf) * (O_HALF * 4 * 64) + lane;
+                (rh * 4 + qq) * (O_Q * 4 * 64) + lane;
 #pragma unroll
-    for (int cb = 0; cb < O_HALF; ++cb) {
+    for (int cb = 0; cb < O_Q; ++cb) {
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
         po[(cb * 4 + qd) * 64] = f32x4{o[cb][4 * qd], o[cb][4 * qd + 1], o[cb][4 * qd + 2], o[cb][4 * qd + 3]};
     }
-    if (hf == 0 && lh == 0) {
-      const float lse2 = l > 0.f ? m_ref + log2f(l) : -INFINITY;
+    const float l = l_run + __shfl_xor(l_run, 32);
+    const float lb = lb_run + __shfl_xor(lb_run, 32);
+    if (lh == 0) {
+      xl[rh][qq][0][lrow] = l;
+      xl[rh][qq][1][lrow] = lb;
+    }
+    __syncthreads();
+    if (qq == 0 && lh == 0) {
+      const float lt = xl[rh][0][0][lrow] + xl[rh][1][0][lrow] + xl[rh][2][0][lrow] + xl[rh][3][0][lrow];
+      const float lbt = xl[rh][0][1][lrow] + xl[rh][1][1][lrow] + xl[rh][2][1][lrow] + xl[rh][3][1][lrow];
+      const float lse2 = lt > 0.f ? m_ref + log2f(lt) : -INFINITY;
       *reinterpret_cast<float2*>(a.part_lse + ((int64_t)w * ROWS + rh * 32 + lrow) * 2) =
-          make_float2(lse2, lb);
+          make_float2(lse2, lbt);
     }
   }
   st |= bad;
@@ -519,13 +532,13 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
 }
 
 // Log-sum-exp merge of the splits.  One block of 256 threads per (request,
-// row group, row half, output-column half, 32-column block, float4 quad):
+// row group, row half, output-column quarter, 32-column block, float4 quad):
 // 32 rows x 8 columns, read as one contiguous 1 KB piece per split.  The
 // threads first turn each split's (lse, weight sum) into the coefficient
 // exp2(lse_s - max) / lb_s of every row; then the 4 waves each accumulate a
 // quarter of the splits and add up through LDS.
 constexpr int RED_THREADS = 256;
-constexpr int RED_PIECES = 2 * 2 * O_HALF * 4;   // blocks per row group
+constexpr int RED_PIECES = 2 * 4 * O_Q * 4;   // blocks per row group
 
 __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   __shared__ float coef[VA_MAX_SPLITS][32];
@@ -545,10 +558,10 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
     ++r;
   }
   const int g = b / RED_PIECES;
-  const int piece = b - g * RED_PIECES;    // ((rh * 2 + hf) * O_HALF + cb) * 4 + qd
-  const int rh = piece / (2 * O_HALF * 4);
-  const int hf = (piece / (O_HALF * 4)) & 1;
-  const int cb = (piece >> 2) % O_HALF;
+  const int piece = b - g * RED_PIECES;    // ((rh * 4 + qq) * O_Q + cb) * 4 + qd
+  const int rh = piece / (4 * O_Q * 4);
+  const int qq = (piece / (O_Q * 4)) & 3;
+  const int cb = (piece >> 2) % O_Q;
   const int qd = piece & 3;
   const int ns = a.nsplit[r];
   const int G = a.num_groups[r];
@@ -625,12 +638,11 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
         lse_out = -INFINITY;
       }
       const int64_t orow = (int64_t)a.tree_begin[r] * H + rr;
-      const int col = hf * (O_HALF * 32) + cb * 32 + 8 * qd + 4 * (lane >> 5);
+      const int col = qq * (O_Q * 32) + cb * 32 + 8 * qd + 4 * (lane >> 5);
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[0]) | ((uint32_t)f32_to_bf16_rne(res[1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[2]) | ((uint32_t)f32_to_bf16_rne(res[3]) << 16);
       *reinterpret_cast<uint2*>(a.out + orow * DV + col) = make_uint2(lo, hi);
-      if (piece == 0 && lane < 32) a.lse[orow] = lse_out;
-      if (piece == 2 * O_HALF * 4 && lane < 32) a.lse[orow] = lse_out;   // rows of row half 1
+      if ((piece & (4 * O_Q * 4 - 1)) == 0 && lane < 32) a.lse[orow] = lse_out;   // once per row
     }
   }
   (void)S;
