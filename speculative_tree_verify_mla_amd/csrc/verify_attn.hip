@@ -48,6 +48,8 @@
 //     weights per row; the reduce normalises, merges a row's splits and
 //     writes bf16 out and natural-log lse.
 #include <hip/hip_runtime.h>
+// m0 is set inside the copy asm (nothing else in these kernels uses it)
+#pragma clang diagnostic ignored "-Winline-asm"
 
 #include <cmath>
 #include <cstdint>
@@ -72,6 +74,7 @@ constexpr int QK_Q = QK_STEPS / 4;    // 9 of them per wave (a quarter of the co
 constexpr int LAT_STEPS = DV / 16;   // the first 32 are latent columns, the last 4 rope
 constexpr int O_Q = DV / 32 / 4;     // 4 MFMA column blocks (32 columns) of the output per wave
 constexpr int PART_VEC = ROWS * DV / 4;  // float4 entries of one work item's partial output
+constexpr int SLOT_RING = 8;         // LDS ring of per-tile slot-table entries (>= 4 live)
 constexpr int MIN_KEYS_PER_SPLIT = 256;
 constexpr float REF_SLACK = 64.f;  // log2 units: probabilities stay <= 2^64
 constexpr int MAX_PASSES = 8;      // restarts of a work item with a raised reference
@@ -156,6 +159,41 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// The partial kernel issues its copies into LDS as inline asm, so the
+// compiler sees no vector-memory operation in the tile loop: it would
+// otherwise make every LDS read wait for all outstanding copies (vmcnt(0)),
+// serialising the copy of tiles t+1, t+2 with the compute of tile t.  The
+// kernel counts its own copies instead (vm_wait) and every wait/barrier is a
+// compiler memory fence.  `nt` marks the KV rows as streamed once.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from sbase + voff (lane i writes lds + 16 i)
+__device__ __forceinline__ void dma16_s(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// 16 bytes per lane from a per-lane address
+__device__ __forceinline__ void dma16_v(uint32_t lds, const void* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(lds), "v"(addr) : "memory", "m0");
+}
+// 4 bytes per lane from a per-lane address (lane i writes lds + 4 i)
+__device__ __forceinline__ void dma4_v(uint32_t lds, const void* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds), "v"(addr) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// barrier that is also a compiler memory fence, after this wave's own LDS
+// operations have completed
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane block,
 // lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
 // i/4, i/4+4, i/4+8 and i/4+12.  A block whose lane i addresses
@@ -184,6 +222,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
   __shared__ u32x2 xp[2][4][64];        // bf16 probabilities [row half][register quad][lane]
   __shared__ float xm[2][4][32];        // per-row values exchanged between the 4 quarter waves
   __shared__ float xl[2][4][2][32];     // per-row sums l, lb of each quarter wave
+  __shared__ int32_t sring[SLOT_RING][TILE];   // slot-table entries of upcoming tiles
   __shared__ uint64_t anc[VA_MAX_TREE];
   __shared__ uint32_t status_sh;
   __shared__ uint32_t restart_sh;
@@ -271,32 +310,42 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     }
   }
 
-  // ---- tile loader.  Lane l holds the slot of key l % 32 of the tile.
-  // Wave w copies the latent rows of keys 4w .. 4w+3 (one 1 KB DMA each);
-  // waves 0..3 also copy the rope parts of keys 8w .. 8w+7 (one DMA).
+  // ---- tile loader.  Wave 4 copies the 32 slot-table entries of tile u into
+  // sring[u % SLOT_RING] (one 4-byte copy per lane; keys past the split end
+  // read the split's last entry, which is in bounds).  For tile u, lane l
+  // takes the slot of key l % 32 from the ring; wave w copies the latent rows
+  // of keys 4w .. 4w+3 (one 1 KB copy each) and waves 0..3 also copy the rope
+  // parts of keys 8w .. 8w+7 (one copy).  Keys past the split end and slots
+  // outside the pool copy the zero row.
   uint32_t bad = 0u;
   const bool rope_wave = wave < 4;
-  auto load_slot = [&](int t) -> int32_t {
-    return table_entry(table, k0 + t * TILE + (lane & 31), k1);
+  const bool slot_wave = wave == 4;
+  auto issue_slots = [&](int u) {
+    if (slot_wave && lane < TILE) {
+      const int k = min(k0 + u * TILE + lane, k1 - 1);
+      dma4_v(lds_addr(&sring[u & (SLOT_RING - 1)][0]), table + k);
+    }
   };
-  auto issue_tile = [&](int t, int32_t vslot, uint16_t* buf) {
-    const int k = k0 + t * TILE + (lane & 31);
+  auto issue_tile = [&](int u, uint16_t* buf) {
+    const int32_t vslot = sring[u & (SLOT_RING - 1)][lane & (TILE - 1)];
+    const int k = k0 + u * TILE + (lane & (TILE - 1));
     const bool exists = k < k1;
     const bool inside = vslot >= 0 && (int64_t)vslot < a.num_slots;
     if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
     const uint64_t use = __ballot(exists && inside);   // bit j: key j of the tile is read
+    const uint32_t lbuf = lds_addr(buf);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = wave * 4 + j;
       const int32_t sj = __builtin_amdgcn_readlane(vslot, key);
       const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sj * a.stride : va_zero_row;
-      dma16(row + lane * 8, buf + key * LAT_STRIDE);
+      dma16_s(lbuf + key * (LAT_STRIDE * 2), row, lane * 16);
     }
     if (rope_wave) {
       const int key = wave * 8 + (lane >> 3);   // key of this lane within the tile
       const int32_t sk = __shfl(vslot, key);
       const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
-      dma16(row + DV + rope_piece(key, lane & 7) * 8, buf + LAT_ELEMS + wave * 8 * DROPE);
+      dma16_v(lbuf + (LAT_ELEMS + wave * 8 * DROPE) * 2, row + DV + rope_piece(key, lane & 7) * 8);
     }
   };
 
@@ -347,8 +396,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
       xs[rh][qq][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
-    wait_lgkmcnt0();   // the LDS writes are done before other waves pass the barrier
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();   // the LDS writes are done before other waves pass the barrier
     // (the own partial is read back too: indexing sacc by the wave's quarter
     // would need register-indexed moves)
     const f32x4 sq0 = xs[rh][0][qq][lane];
@@ -374,8 +422,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     if (first) {
       // reference = the row's max over the whole tile (all 4 quads)
       if (lh == 0) xm[rh][qq][lrow] = mx;
-      wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();
+      lds_barrier();
       const float r4 = fmaxf(fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]),
                              fmaxf(xm[rh][2][lrow], xm[rh][3][lrow]));
       if (m_ref == -INFINITY) m_ref = r4;
@@ -398,8 +445,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     l_run += (p[0] + p[1]) + (p[2] + p[3]);
     lb_run = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, __builtin_amdgcn_fdot2_f32_bf16(p01, ones, lb_run, false), false);
     xp[rh][qq][lane] = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     // B operand of k-step ks: the probabilities of quads 2ks and 2ks+1
     bf16x8 pf[2];
 #pragma unroll
@@ -432,13 +478,16 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- pipeline.  Per wave, the vector-memory ops are issued in the order
-  // [slots(u+1), DMA(u)] for u = 0, 1, 2, ...; they complete in order, so
-  // once the copies of DMA(t+1) have been issued after DMA(t), "at most that
-  // many outstanding" means DMA(t) has landed in LDS (the slots of t+2,
-  // issued a whole tile earlier, are waited for with it).  Buffer t % 3
-  // holds tile t; DMA(t+2) is issued after the barrier that ends every
-  // wave's use of tile t-1, the buffer's previous content.
+  // ---- pipeline over the split's tiles.  Buffer u % 3 holds tile u.  Per
+  // wave the copies are issued in the order
+  //   [slots 0, 1] (wait) [tile 0, slots 2] [tile 1, slots 3] | loop t: [tile t+2, slots t+4]
+  // (slot copies on wave 4 only, rope copies on waves 0..3), and vmcnt
+  // counts them in issue order.  At the top of iteration t each wave waits
+  // until only the copies issued after its part of tile t+1 are left; wave 4
+  // also needs slots t+2, issued right after tile t, so it keeps at most
+  // tile t+1 and slots t+3 outstanding.  The barrier then publishes tile t
+  // and slots t+2 to every wave and ends all use of tile t-1, whose buffer
+  // tile t+2 overwrites.
   uint64_t anc_row = 0ull;
   for (int pass = 0;; ++pass) {
 #pragma unroll
@@ -449,44 +498,44 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     l_run = 0.f;
     lb_run = 0.f;
     if (tid == 0) restart_sh = 0u;
-    int32_t slot_next = 0;
     if (ntiles > 0) {
-      const int32_t s0 = load_slot(0);
-      slot_next = load_slot(ntiles > 1 ? 1 : 0);
-      issue_tile(0, s0, tiles);
-      if (ntiles > 1) {
-        const int32_t s1 = slot_next;
-        slot_next = load_slot(ntiles > 2 ? 2 : 1);
-        issue_tile(1, s1, tiles + BUF_ELEMS);
-      }
+      issue_slots(0);
+      issue_slots(1);
     }
-    __syncthreads();   // anc[], status_sh and restart_sh ready
+    // compiler-visible wait: also completes the Q loads, so the compiler adds
+    // no wait of its own before their first use
+    wait_vmcnt<0>();
+    __syncthreads();   // slots 0, 1, anc[], status_sh and restart_sh ready
     if (pass == 0) anc_row = row_ok ? anc[rho / H] : 0ull;
+    if (ntiles > 0) {
+      issue_tile(0, tiles);
+      issue_slots(2);
+      if (ntiles > 1) issue_tile(1, tiles + BUF_ELEMS);
+      issue_slots(3);
+    }
 
     int cur_buf = 0;   // tile t lives in buffer t % 3
     bool restart = false;
     for (int t = 0; t < ntiles; ++t) {
       if (t + 1 < ntiles) {
-        if (rope_wave) wait_vmcnt<5>(); else wait_vmcnt<4>();   // this wave's copies per tile
+        if (rope_wave) vm_wait<5>(); else if (slot_wave) vm_wait<5>(); else vm_wait<4>();
       } else {
-        wait_vmcnt<0>();
+        if (slot_wave) vm_wait<1>(); else vm_wait<0>();
       }
-      __builtin_amdgcn_s_barrier();   // tile t is in LDS; every wave is done with tile t-1
+      lds_barrier();   // tile t is in LDS; every wave is done with tile t-1
       if (restart_sh != 0u && pass + 1 < MAX_PASSES) {   // uniform: read after the barrier
         restart = true;
         break;
       }
       if (t + 2 < ntiles) {
-        const int32_t sl = slot_next;
-        slot_next = load_slot(t + 3 < ntiles ? t + 3 : t + 2);
         const int later = cur_buf == 0 ? 2 : cur_buf - 1;   // (t + 2) % 3
-        issue_tile(t + 2, sl, tiles + later * BUF_ELEMS);
+        issue_tile(t + 2, tiles + later * BUF_ELEMS);
       }
+      issue_slots(t + 4);
       compute(t, tiles + cur_buf * BUF_ELEMS, anc_row, t == 0);
-      wait_lgkmcnt0();
       cur_buf = cur_buf == 2 ? 0 : cur_buf + 1;
     }
-    wait_vmcnt<0>();
+    vm_wait<0>();
     __syncthreads();   // all copies landed and all waves are done with the tiles
     if (!restart) restart = restart_sh != 0u && pass + 1 < MAX_PASSES;
     if (!restart) break;
@@ -531,21 +580,25 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
   if (tid == 0) a.status[w] = status_sh;
 }
 
-// Log-sum-exp merge of the splits.  One block of 256 threads per (request,
+// Log-sum-exp merge of the splits.  One block of 512 threads per (request,
 // row group, row half, output-column quarter, 32-column block, float4 quad):
 // 32 rows x 8 columns, read as one contiguous 1 KB piece per split.  The
 // threads first turn each split's (lse, weight sum) into the coefficient
-// exp2(lse_s - max) / lb_s of every row; then the 4 waves each accumulate a
-// quarter of the splits and add up through LDS.
-constexpr int RED_THREADS = 256;
+// exp2(lse_s - max) / lb_s of every row; then the 8 waves each accumulate an
+// eighth of the splits, 8 independent 1 KB loads at a time, and add up
+// through LDS.
+constexpr int RED_THREADS = 512;
+constexpr int RED_WAVES = RED_THREADS / 64;
+constexpr int RED_SG = RED_THREADS / 32;      // split groups of the coefficient pass
+constexpr int RED_UNROLL = 8;
 constexpr int RED_PIECES = 2 * 4 * O_Q * 4;   // blocks per row group
 
 __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   __shared__ float coef[VA_MAX_SPLITS][32];
-  __shared__ float red_m[8][32];
-  __shared__ float red_w[8][32];
-  __shared__ uint32_t red_s[8][32];
-  __shared__ f32x4 part[4][64];
+  __shared__ float red_m[RED_SG][32];
+  __shared__ float red_w[RED_SG][32];
+  __shared__ uint32_t red_s[RED_SG][32];
+  __shared__ f32x4 part[RED_WAVES][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -572,27 +625,25 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   // per-row max and weight sums over the splits: thread = (split group sg, row)
   const int row = tid & 31;
   const int sg = tid >> 5;
+  const float2* plse = reinterpret_cast<const float2*>(a.part_lse) + wbase * ROWS + rh * 32 + row;
   float m = -INFINITY;
   uint32_t st = 0u;
-  for (int s = sg; s < ns; s += 8) {
+#pragma unroll 4
+  for (int s = sg; s < ns; s += RED_SG) {
     const int64_t w = wbase + (int64_t)s * G;
-    m = fmaxf(m, a.part_lse[(w * ROWS + rh * 32 + row) * 2]);
+    m = fmaxf(m, plse[(int64_t)s * G * ROWS].x);
     st |= a.status[w];
   }
   red_m[sg][row] = m;
   red_s[sg][row] = st;
   __syncthreads();
   float M = red_m[0][row];
-  uint32_t S = red_s[0][row];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    M = fmaxf(M, red_m[i][row]);
-    S |= red_s[i][row];
-  }
+  for (int i = 1; i < RED_SG; ++i) M = fmaxf(M, red_m[i][row]);
   float wsum = 0.f;
-  for (int s = sg; s < ns; s += 8) {
-    const int64_t w = wbase + (int64_t)s * G;
-    const float2 v = *reinterpret_cast<const float2*>(a.part_lse + (w * ROWS + rh * 32 + row) * 2);
+#pragma unroll 4
+  for (int s = sg; s < ns; s += RED_SG) {
+    const float2 v = plse[(int64_t)s * G * ROWS];
     const float e = (v.x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(v.x - M);
     wsum += e;
     coef[s][row] = (e > 0.f && v.y > 0.f) ? e / v.y : 0.f;
@@ -600,28 +651,42 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   red_w[sg][row] = wsum;
   __syncthreads();
 
-  // weighted sum of this block's 1 KB piece over the splits
+  // weighted sum of this block's 1 KB piece over the splits (a split whose
+  // coefficient is 0 adds nothing, whatever its partial holds)
   const int prow = lane & 31;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o) + piece * 64 + lane;
-  for (int s = wave; s < ns; s += 4) {
-    const float c = coef[s][prow];
-    if (c != 0.f) acc += c * src[(wbase + (int64_t)s * G) * PART_VEC];
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o) + wbase * PART_VEC + piece * 64 + lane;
+  const int64_t split_step = (int64_t)G * PART_VEC;
+  for (int s0 = wave; s0 < ns; s0 += RED_WAVES * RED_UNROLL) {
+    f32x4 v[RED_UNROLL];
+    float c[RED_UNROLL];
+#pragma unroll
+    for (int u = 0; u < RED_UNROLL; ++u) {
+      const int s = s0 + u * RED_WAVES;
+      const bool in = s < ns;
+      c[u] = in ? coef[s][prow] : 0.f;
+      v[u] = in ? src[(int64_t)s * split_step] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < RED_UNROLL; ++u) {
+      if (c[u] != 0.f) acc += c[u] * v[u];
+    }
   }
   part[wave][lane] = acc;
   __syncthreads();
   if (tid < 64) {
-    const f32x4 tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    f32x4 tot = part[0][lane];
+#pragma unroll
+    for (int i = 1; i < RED_WAVES; ++i) tot += part[i][lane];
     float W = 0.f;
     uint32_t Sr = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      W += red_w[i][prow];
-      Sr |= red_s[i][prow];
-    }
     float Mr = red_m[0][prow];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) Mr = fmaxf(Mr, red_m[i][prow]);
+    for (int i = 0; i < RED_SG; ++i) {
+      W += red_w[i][prow];
+      Sr |= red_s[i][prow];
+      Mr = fmaxf(Mr, red_m[i][prow]);
+    }
     const int rr = g * ROWS + rh * 32 + prow;   // row within the request
     if (rr < rows_r) {
       float res[4];
@@ -645,7 +710,6 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
       if ((piece & (4 * O_Q * 4 - 1)) == 0 && lane < 32) a.lse[orow] = lse_out;   // once per row
     }
   }
-  (void)S;
 }
 
 // Diagnostic: pool rows through the partial pass's table/slot checks and its
