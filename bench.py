@@ -22,8 +22,10 @@ the host cores, full verify calls repeated for a bounded ~10-30 s.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,6 +41,31 @@ WORKLOAD = 3                   # 1 request, H=8, T=16, L=65536
 N_POOLS = 8
 
 
+KERNEL_SRC = os.path.join(ROOT, "speculative_tree_verify_mla_amd", "csrc", "verify_attn.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_va_partial_kernel_tp_rank_h8_t16_l65536.txt")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile():
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None
+    when there is no summary or it was taken on another version of the kernel
+    source."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    sha = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not sha or not val or sha.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -51,6 +78,8 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--eager", action="store_true", help="launch without graph capture")
+    ap.add_argument("--no-stream-peak", action="store_true",
+                    help="skip the 2 GiB streaming-read calibration")
     return ap.parse_args()
 
 
@@ -159,6 +188,22 @@ def main():
         torch.cuda.synchronize()
         print(f"# calibration copy of {nbytes} bytes x3 done", file=sys.stderr, flush=True)
 
+    stream_peak = None
+    if not args.no_stream_peak:
+        # measured read ceiling of this GPU: a plain torch reduction over 2 GiB
+        big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+        big.sum()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            big.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        stream_peak = big.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del big
+
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
@@ -181,6 +226,7 @@ def main():
         parity = {"max_abs_out": float(np.abs(got - ref).max()),
                   "max_abs_lse": float(np.abs(lse.cpu().numpy() - ref_lse).max())}
 
+    traffic = traffic_from_profile()
     result = {
         "metric": "effective KV GB/s (% HBM peak) + us/verify call @65k prefix, H=8, T=16",
         "value": round(gbs, 2),
@@ -203,6 +249,8 @@ def main():
         },
         "us_per_call": round(ms_per_step * 1e3, 3),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "stream_read_peak_gbs": None if stream_peak is None else round(stream_peak, 1),
+        "pct_stream_read_peak": None if stream_peak is None else round(100.0 * gbs / stream_peak, 2),
         "mfma_util_pct": round(100.0 * flops / (ms_per_step * 1e-3) / 1e12
                                / BF16_DENSE_PEAK_TFLOPS, 2),
         "warm_us_per_call": round(ms_warm * 1e3, 3),
@@ -217,7 +265,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs_partial / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_us": round(ms_partial * 1e3, 3),
             "warm_avg_us": round(ms_partial_warm * 1e3, 3),
         },

@@ -12,33 +12,33 @@
 //
 // gfx950 mapping of one work item (request r, row group g of 64 query rows,
 // KV split s):
-//   - 256 threads = 4 wave64s.  Wave w owns rows 32*(w&1) .. +31 of the row
-//     group (two 16-row MFMA blocks, so every 16-byte LDS fragment feeds two
-//     MFMAs and the LDS read rate matches the MFMA rate) and half h = w>>1 of
-//     the work: the score columns 288*h .. +287 and the output columns
-//     256*h .. +255.  The two waves of a row half add their partial scores
-//     through LDS, then both run the same softmax on the full scores.
+//   - 512 threads = 8 wave64s, two per SIMD.  Wave w owns row half
+//     rh = w & 1 (32 query rows, the MFMA N dimension) and quarter
+//     qq = w >> 1 of the work: score columns 144*qq .. +143, the probabilities
+//     of keys 8*qq .. +7 of each 32-key tile (one register quad), and output
+//     columns 128*qq .. +127.  Partial scores, bf16 probabilities and, on a
+//     pass's first tile, the row maxima are exchanged through LDS.
 //   - Tiles of 32 pool rows go straight from HBM into LDS with
 //     global_load_lds_dwordx4 (1 KB per wave instruction), triple-buffered:
-//     the next two tiles are in flight while one is consumed.  Slot indices
-//     are fetched a tile ahead of their rows.  The latent part of a row is
-//     stored with a 1072-byte pitch and the rope part XOR-swizzled, so both
-//     MFMA read patterns below are free of LDS bank conflicts.
+//     two tiles are in flight while one is consumed.  The slot-table entries
+//     of a tile are copied into a small LDS ring two tiles ahead of its rows.
+//     All these copies are inline asm counted by hand (see vm_wait), so the
+//     compiler never makes an LDS read wait for them.  The latent part of a
+//     row is stored with a 1072-byte pitch and the rope part XOR-swizzled, so
+//     both MFMA read patterns below are free of LDS bank conflicts.
 //   - S^T[key][row] = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K fragment
 //     from LDS, B = Q rows held in VGPRs; the 32x32 shape runs near the
 //     dense bf16 peak, the 16x16 one at about a third of it).  The output
-//     layout gives each lane one query row (lane % 32) and 16 of its 32
-//     keys, so the row max needs one cross-lane step, and the probabilities
-//     of keys 16*ks .. +15 are already, register for register, the B operand
-//     of O^T = V^T . P^T for k-step ks.  That operand's A side comes from the
-//     same K tile through ds_read_b64_tr_b16 (transpose reads: no transposed
-//     copy of V).
+//     layout gives each lane one query row (lane % 32) and, per register
+//     quad, 4 of the tile's keys, so the probabilities of keys 16*ks .. +15
+//     are, register for register, the B operand of O^T = V^T . P^T for
+//     k-step ks.  That operand's A side comes from the same K tile through
+//     ds_read_b64_tr_b16 (transpose reads: no transposed copy of V).
 //   - Each row's probabilities are taken against a fixed reference: the
 //     row's first finite tile max.  Probabilities may then exceed 1 (up to
 //     2^64), which bf16 and the fp32 accumulators hold without loss of
-//     relative precision, and the accumulators are never rescaled, so they
-//     stay in the MFMA accumulator registers for the whole pass.  If a later
-//     tile beats a row's reference by more than 2^64 (only adversarial
+//     relative precision, and the accumulators are never rescaled.  If a
+//     later tile beats a row's reference by more than 2^64 (only adversarial
 //     inputs do), the work item restarts from its first tile with the
 //     reference raised to the largest max seen.
 //   - The tree mask is one 64-bit ancestor mask per draft node, built in the
@@ -47,6 +47,7 @@
 //     layout (1 KB per wave store), lse (base 2) and the sum of its bf16
 //     weights per row; the reduce normalises, merges a row's splits and
 //     writes bf16 out and natural-log lse.
+
 #include <hip/hip_runtime.h>
 // m0 is set inside the copy asm (nothing else in these kernels uses it)
 #pragma clang diagnostic ignored "-Winline-asm"

@@ -184,6 +184,30 @@ def test_pool_permutation_invariance():
     assert np.abs(out3 - out).max() > 1e-3
 
 
+def test_duplicate_slots_count_once_per_table_entry():
+    """Two table entries naming one slot act as two keys with the same row:
+    pointing the second entry at a fresh slot holding a copy changes nothing."""
+    wl = inputs.make_workload("dup", 2, [4], [30], 128, seed=44)
+    table = wl.slot_table.copy()
+    table[7] = table[3]                                     # duplicate a prefix slot
+    used = set(int(x) for x in table)
+    fresh = next(s for s in range(wl.num_slots) if s not in used)
+    pool2 = wl.kv_pool.copy()
+    pool2[fresh] = wl.kv_pool[table[3]]
+    table2 = table.copy()
+    table2[7] = fresh
+    args = (wl.num_heads, wl.num_tree, wl.prefix_len, wl.q)
+    out, lse = oracle.verify_attn(*args, wl.kv_pool, table, wl.slot_indptr, wl.parent, SM)
+    out2, lse2 = oracle.verify_attn(*args, pool2, table2, wl.slot_indptr, wl.parent, SM)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+    # the duplicate is a real second key: dropping it (pointing it elsewhere) changes lse
+    table3 = table.copy()
+    table3[7] = wl.slot_table[7]
+    _, lse3 = oracle.verify_attn(*args, wl.kv_pool, table3, wl.slot_indptr, wl.parent, SM)
+    assert np.abs(lse3 - lse).max() > 1e-6
+
+
 def test_probabilities_normalised_and_masked_exactly_zero():
     wl = inputs.make_workload("probs", 2, [12], [20], 128, seed=43)
     out, lse, p = oracle.verify_attn_workload(wl, return_probs=True)
