@@ -91,7 +91,7 @@ typedef struct va_plan {
   int32_t num_requests;      /* B */
   int32_t num_heads;         /* H */
   int32_t rows_per_group;    /* query rows (node, head) one work item holds */
-  int32_t tile_keys;         /* keys per KV tile; split lengths are multiples of it */
+  int32_t tile_keys;         /* keys per KV tile; split lengths are multiples of half of it */
   int32_t total_work;        /* work items of the partial pass (its grid) */
   int32_t total_tree;        /* sum of T_r */
   int32_t total_rows;        /* sum of T_r * H */

@@ -20,10 +20,6 @@ HIPCC_FLAGS = [
     "-fPIC",
     # keep hipcc from forming packed fp32 instructions on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in arch VGPRs: with the default heuristic the
-    # loop-carried output accumulators bounce between AGPRs and VGPRs on
-    # every KV tile of the partial kernel
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -12,28 +12,30 @@
 //
 // gfx950 mapping of one work item (request r, row group g of 64 query rows,
 // KV split s):
-//   - 512 threads = 8 wave64s, two per SIMD.  Wave w owns row half
-//     rh = w & 1 (32 query rows, the MFMA N dimension) and quarter
-//     qq = w >> 1 of the work: score columns 144*qq .. +143, the probabilities
-//     of keys 8*qq .. +7 of each 32-key tile (one register quad), and output
-//     columns 128*qq .. +127.  Partial scores, bf16 probabilities and, on a
-//     pass's first tile, the row maxima are exchanged through LDS.
-//   - Tiles of 32 pool rows go straight from HBM into LDS with
-//     global_load_lds_dwordx4 (1 KB per wave instruction), triple-buffered:
-//     two tiles are in flight while one is consumed.  The slot-table entries
-//     of a tile are copied into a small LDS ring two tiles ahead of its rows.
-//     All these copies are inline asm counted by hand (see vm_wait), so the
-//     compiler never makes an LDS read wait for them.  The latent part of a
-//     row is stored with a 1072-byte pitch and the rope part XOR-swizzled, so
-//     both MFMA read patterns below are free of LDS bank conflicts.
+//   - 256 threads = 4 wave64s, one per SIMD.  Wave w owns row half
+//     rh = w & 1 (32 query rows, the MFMA N dimension) and half kh = w >> 1
+//     of the work: for the score, keys 32*kh .. +31 of every 64-key tile over
+//     all 576 columns (the full Q of its rows stays in VGPRs, so no partial
+//     scores are exchanged); for the output, columns 256*kh .. +255 over all
+//     64 keys.  The two key halves hand each other their bf16 probabilities
+//     through an 8 KB LDS buffer: one barrier per tile besides the tile
+//     barrier.
+//   - Tiles of 64 pool rows go straight from HBM into LDS with
+//     global_load_lds_dwordx4 (1 KB per wave instruction), double-buffered:
+//     one tile is in flight while the other is consumed.  The slot-table
+//     entries of a tile are copied into a small LDS ring two tiles ahead of
+//     its rows.  All these copies are inline asm counted by hand (see
+//     vm_wait), so the compiler never makes an LDS read wait for them.  The
+//     latent part of a row is stored with a 1072-byte pitch and the rope part
+//     XOR-swizzled, so both MFMA read patterns below are free of LDS bank
+//     conflicts.
 //   - S^T[key][row] = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K fragment
-//     from LDS, B = Q rows held in VGPRs; the 32x32 shape runs near the
-//     dense bf16 peak, the 16x16 one at about a third of it).  The output
-//     layout gives each lane one query row (lane % 32) and, per register
-//     quad, 4 of the tile's keys, so the probabilities of keys 16*ks .. +15
-//     are, register for register, the B operand of O^T = V^T . P^T for
-//     k-step ks.  That operand's A side comes from the same K tile through
-//     ds_read_b64_tr_b16 (transpose reads: no transposed copy of V).
+//     from LDS, B = Q rows held in VGPRs).  The output layout gives each lane
+//     one query row (lane % 32) and, per register quad, 4 of the wave's keys,
+//     so the probabilities of keys 16*ks .. +15 are, register for register,
+//     the B operand of O^T = V^T . P^T for k-step ks.  That operand's A side
+//     comes from the same K tile through ds_read_b64_tr_b16 (transpose reads:
+//     no transposed copy of V).
 //   - Each row's probabilities are taken against a fixed reference: the
 //     row's first finite tile max.  Probabilities may then exceed 1 (up to
 //     2^64), which bf16 and the fp32 accumulators hold without loss of
@@ -43,10 +45,10 @@
 //     reference raised to the largest max seen.
 //   - The tree mask is one 64-bit ancestor mask per draft node, built in the
 //     prologue from parent[]; only tiles reaching past the prefix consult it.
-//   - Each work item writes its unnormalised accumulators in the MFMA output
-//     layout (1 KB per wave store), lse (base 2) and the sum of its bf16
-//     weights per row; the reduce normalises, merges a row's splits and
-//     writes bf16 out and natural-log lse.
+//   - Each work item writes its normalised output o / lb (lb = the sum of the
+//     bf16 weights) in fp16 with a per-row power-of-two scale, in the MFMA
+//     output layout (512 B per wave store), and its lse (base 2); the reduce
+//     merges a row's splits and writes bf16 out and natural-log lse.
 
 #include <hip/hip_runtime.h>
 // m0 is set inside the copy asm (nothing else in these kernels uses it)
@@ -64,18 +66,22 @@ namespace {
 constexpr int DQK = VA_D_QK;      // 576
 constexpr int DV = VA_D_V;        // 512: value columns = latent columns
 constexpr int DROPE = DQK - DV;   // 64 rope columns
-constexpr int TILE = 32;          // keys per LDS tile
-constexpr int THREADS = 512;      // 8 waves, 2 per SIMD
+constexpr int TILE = 64;          // keys per LDS tile
+constexpr int HALF = TILE / 2;    // keys of a tile one wave owns (the MFMA M dimension)
+constexpr int SPLIT_ALIGN = 32;   // split lengths are multiples of this many keys
+constexpr int THREADS = 256;      // 4 waves, one per SIMD
 constexpr int ROWS = 64;          // query rows per work item
 constexpr int LAT_STRIDE = DV + 24;               // bf16 per latent row in LDS (1072 B)
 constexpr int LAT_ELEMS = TILE * LAT_STRIDE;
-constexpr int BUF_ELEMS = LAT_ELEMS + TILE * DROPE;  // one tile buffer: 38,400 B
+constexpr int BUF_ELEMS = LAT_ELEMS + TILE * DROPE;  // one tile buffer: 76,800 B
 constexpr int QK_STEPS = DQK / 16;   // 36 MFMA k-steps (16 columns each) for the score
-constexpr int QK_Q = QK_STEPS / 4;    // 9 of them per wave (a quarter of the columns)
 constexpr int LAT_STEPS = DV / 16;   // the first 32 are latent columns, the last 4 rope
-constexpr int O_Q = DV / 32 / 4;     // 4 MFMA column blocks (32 columns) of the output per wave
-constexpr int PART_VEC = ROWS * DV / 4;  // float4 entries of one work item's partial output
-constexpr int SLOT_RING = 8;         // LDS ring of per-tile slot-table entries (>= 4 live)
+constexpr int O_BLK = DV / 32;       // 16 MFMA column blocks (32 columns) of the output
+constexpr int O_HALF = O_BLK / 2;    // 8 of them per wave (one column half)
+constexpr int PART_VEC = ROWS * DV / 4;  // 4-column entries of one work item's partial output
+constexpr int SLOT_RING = 4;         // LDS ring of per-tile slot-table entries (3 live)
+constexpr int LAT_DMA = TILE / 4;    // latent rows one wave copies per tile
+constexpr int ROPE_DMA = TILE / 32;  // rope blocks (8 keys each) one wave copies per tile
 constexpr int MIN_KEYS_PER_SPLIT = 256;
 constexpr float REF_SLACK = 64.f;  // log2 units: probabilities stay <= 2^64
 constexpr int MAX_PASSES = 8;      // restarts of a work item with a raised reference
@@ -87,6 +93,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -105,8 +112,8 @@ struct PartialArgs {
   const int32_t* slot_indptr;
   const int32_t* prefix_len;
   const int32_t* parent;
-  float* part_o;      // [work][PART_VEC] f32x4, unnormalised, MFMA layout (see the reduce)
-  float* part_lse;    // [work][ROWS][2]: lse (base 2), sum of bf16 weights
+  uint32_t* part_o;   // [work][PART_VEC] 4 x fp16 (o / lb scaled by 2^-e), MFMA layout
+  float* part_lse;    // [work][ROWS][2]: lse (base 2), scale exponent e
   uint32_t* status;   // [work]
   int32_t num_tree[VA_MAX_REQUESTS];
   int32_t max_prefix[VA_MAX_REQUESTS];
@@ -117,8 +124,8 @@ struct PartialArgs {
 };
 
 struct ReduceArgs {
-  const float* part_o;
-  const float* part_lse;   // [work][ROWS][2]: lse (base 2), sum of bf16 weights
+  const uint32_t* part_o;  // [work][PART_VEC] 4 x fp16 (o / lb scaled by 2^-e), MFMA layout
+  const float* part_lse;   // [work][ROWS][2]: lse (base 2), scale exponent e
   const uint32_t* status;
   uint16_t* out;
   float* lse;
@@ -218,21 +225,22 @@ __device__ __forceinline__ int32_t table_entry(const int32_t* __restrict__ table
 __device__ __forceinline__ int rope_piece(int key, int piece) { return piece ^ ((key >> 1) & 7); }
 
 __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[3 * BUF_ELEMS];
-  __shared__ f32x4 xs[2][4][4][64];     // partial scores [row half][quarter][register quad][lane]
-  __shared__ u32x2 xp[2][4][64];        // bf16 probabilities [row half][register quad][lane]
-  __shared__ float xm[2][4][32];        // per-row values exchanged between the 4 quarter waves
-  __shared__ float xl[2][4][2][32];     // per-row sums l, lb of each quarter wave
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2 * BUF_ELEMS];
+  // bf16 probabilities [row half][key half][lane] (two value-MFMA operands per
+  // lane); before the first tile the same bytes hold the ancestor masks
+  __shared__ __attribute__((aligned(16))) bf16x8 xp[2][2][2][64];
   __shared__ int32_t sring[SLOT_RING][TILE];   // slot-table entries of upcoming tiles
-  __shared__ uint64_t anc[VA_MAX_TREE];
+  __shared__ float xm[2][2][32];               // per-row maxima [row half][key half][row]
   __shared__ uint32_t status_sh;
   __shared__ uint32_t restart_sh;
+  uint64_t* anc = reinterpret_cast<uint64_t*>(&xp[0][0][0][0]);   // [VA_MAX_TREE]
+  static_assert(sizeof(xp) >= VA_MAX_TREE * sizeof(uint64_t), "ancestor masks fit");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = wave & 1;      // row half of the work item's 64 rows
-  const int qq = wave >> 1;     // quarter: score columns, register quad (keys), output columns
+  const int kh = wave >> 1;     // key half of every tile for the score; column half of the output
   const int lrow = lane & 31;   // MFMA column: this lane's query row within the row half
   const int lh = lane >> 5;     // MFMA k-half of this lane
 
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     n_valid = (tab0 < 0 || tab1 < tab0 || tab0 >= a.slot_table_len)
                   ? 0 : min(min(tab1, a.slot_table_len) - tab0, n);
   }
-  const int chunk = ((n + ns - 1) / ns + TILE - 1) / TILE * TILE;
+  const int chunk = ((n + ns - 1) / ns + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
   const int k0 = s * chunk;
   const int k1 = min(n_valid, k0 + chunk);   // end of this split (keys past a short table dropped)
   const int ntiles = k1 > k0 ? (k1 - k0 + TILE - 1) / TILE : 0;
@@ -296,203 +304,236 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     anc[tid] = m;
   }
 
-  // ---- Q fragments of this lane's row over this wave's 144 score columns
+  // ---- Q fragments of this lane's row over all 576 score columns
   const int rho = g * ROWS + rh * 32 + lrow;
   const bool row_ok = rho < rows_r;
-  bf16x8 qf[QK_Q];
+  bf16x8 qf[QK_STEPS];
   {
     const int64_t qrow = (int64_t)a.tree_begin[r] * H + (row_ok ? rho : 0);
-    const uint16_t* qp = a.q + qrow * DQK + qq * (QK_Q * 16) + lh * 8;
+    const uint16_t* qp = a.q + qrow * DQK + lh * 8;
 #pragma unroll
-    for (int k = 0; k < QK_Q; ++k) {
+    for (int k = 0; k < QK_STEPS; ++k) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qp + k * 16);
       if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
       qf[k] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  // ---- tile loader.  Wave 4 copies the 32 slot-table entries of tile u into
+  // ---- tile loader.  Wave 0 copies the 64 slot-table entries of tile u into
   // sring[u % SLOT_RING] (one 4-byte copy per lane; keys past the split end
   // read the split's last entry, which is in bounds).  For tile u, lane l
-  // takes the slot of key l % 32 from the ring; wave w copies the latent rows
-  // of keys 4w .. 4w+3 (one 1 KB copy each) and waves 0..3 also copy the rope
-  // parts of keys 8w .. 8w+7 (one copy).  Keys past the split end and slots
-  // outside the pool copy the zero row.
+  // takes the slot of key l from the ring; wave w copies the latent rows of
+  // keys 16w .. 16w+15 (one 1 KB copy each) and the rope parts of the same
+  // keys (two copies of 8 rows).  Keys past the split end and slots outside
+  // the pool copy the zero row.
   uint32_t bad = 0u;
-  const bool rope_wave = wave < 4;
-  const bool slot_wave = wave == 4;
   auto issue_slots = [&](int u) {
-    if (slot_wave && lane < TILE) {
+    if (wave == 0) {
       const int k = min(k0 + u * TILE + lane, k1 - 1);
       dma4_v(lds_addr(&sring[u & (SLOT_RING - 1)][0]), table + k);
     }
   };
   auto issue_tile = [&](int u, uint16_t* buf) {
-    const int32_t vslot = sring[u & (SLOT_RING - 1)][lane & (TILE - 1)];
-    const int k = k0 + u * TILE + (lane & (TILE - 1));
+    const int32_t vslot = sring[u & (SLOT_RING - 1)][lane];
+    const int k = k0 + u * TILE + lane;
     const bool exists = k < k1;
     const bool inside = vslot >= 0 && (int64_t)vslot < a.num_slots;
     if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
     const uint64_t use = __ballot(exists && inside);   // bit j: key j of the tile is read
     const uint32_t lbuf = lds_addr(buf);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = wave * 4 + j;
+    for (int j = 0; j < LAT_DMA; ++j) {
+      const int key = wave * LAT_DMA + j;
       const int32_t sj = __builtin_amdgcn_readlane(vslot, key);
       const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sj * a.stride : va_zero_row;
       dma16_s(lbuf + key * (LAT_STRIDE * 2), row, lane * 16);
     }
-    if (rope_wave) {
-      const int key = wave * 8 + (lane >> 3);   // key of this lane within the tile
+#pragma unroll
+    for (int j = 0; j < ROPE_DMA; ++j) {
+      const int kb = (wave * ROPE_DMA + j) * 8;   // first key of this rope block
+      const int key = kb + (lane >> 3);          // key of this lane
       const int32_t sk = __shfl(vslot, key);
       const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
-      dma16_v(lbuf + (LAT_ELEMS + wave * 8 * DROPE) * 2, row + DV + rope_piece(key, lane & 7) * 8);
+      dma16_v(lbuf + (LAT_ELEMS + kb * DROPE) * 2, row + DV + rope_piece(key, lane & 7) * 8);
     }
   };
 
-  f32x16 o[O_Q];
+  f32x16 o[O_HALF];
   // The reference this row's probabilities are taken against (common to the
-  // 4 quarter waves), the largest tile max this wave has seen, and partial
-  // sums over this wave's keys (the other half of the quad's keys is on lane
-  // ^ 32).  l sums the fp32 probabilities and gives the lse; lb sums the bf16
-  // probabilities that enter the value MFMA and normalises the output, so the
-  // output is an exact weighted average of its value rows.
+  // two key-half waves of a row half), the largest tile max this wave has
+  // seen, and the sums over this wave's keys (lane ^ 32 holds the other
+  // half of the row's keys).  l sums the fp32 probabilities and gives the
+  // lse; lb sums the bf16 probabilities that enter the value MFMA and
+  // normalises the output, so the output is an exact weighted average of its
+  // value rows.
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;
   float l_run = 0.f;
   float lb_run = 0.f;
 
   // per-lane LDS element offsets of the MFMA operands within a tile buffer
-  const int k_lat = lrow * LAT_STRIDE + lh * 8;        // K fragment, latent k-steps
-  const int k_rope = LAT_ELEMS + lrow * DROPE;          // K fragment row, rope k-steps 32..35
-  // value operand: block b = lane/16 of the wave reads keys 4*(b>>1) + i/4
-  // (+8) and columns 16*(b&1) + 4*(i%4) of each 32-column block (i = lane%16)
+  const int krow = kh * HALF + lrow;                      // this lane's key row for the score
+  const int k_lat = krow * LAT_STRIDE + lh * 8;           // K fragment, latent k-steps
+  const int k_rope = LAT_ELEMS + krow * DROPE;            // K fragment row, rope k-steps 32..35
+  // value operand: block b = lane/16 reads keys 16*ks + 4*(b>>1) + i/4 (+8)
+  // and columns 16*(b&1) + 4*(i%4) of each 32-column block (i = lane%16) of
+  // this wave's column half
   const int v_off = (4 * lh + ((lane & 15) >> 2)) * LAT_STRIDE + 16 * ((lane >> 4) & 1) +
-                    4 * (lane & 3) + qq * (O_Q * 32);
-  // this wave's register quad: keys 8*qq + 4*lh + i of the tile
-  const int qkey = 8 * qq + 4 * lh;
+                    4 * (lane & 3) + kh * (O_HALF * 32);
+  const int qkey = kh * HALF + 4 * lh;   // tile key of register 4*qd+i is qkey + 8*qd + i
 
   // Consumes tile t (one buffer).  `first` is set on the first tile of a
-  // pass: the quarter waves then agree on each row's reference.
+  // pass: the two key-half waves then agree on each row's reference.
   auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row, bool first) {
     const int kt = k0 + t * TILE;
-    // partial S^T = K . Q^T over this wave's 144 score columns
+    // a key half lying wholly past the split end contributes zero weights
+    // (uniform; the first tile still joins the reference exchange)
+    const bool empty = kt + kh * HALF >= k1;
+    if (empty && !first) {
+      xp[rh][kh][0][lane] = bf16x8{};
+      xp[rh][kh][1][lane] = bf16x8{};
+      return;
+    }
+    // S^T = K . Q^T for this wave's 32 keys over all 576 score columns
     f32x16 sacc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-    bf16x8 kf[QK_Q];
+    // K fragments in groups of QG k-steps, the next group's LDS reads issued
+    // ahead of the current group's MFMAs
+    constexpr int QG = 6;
+    auto load_k = [&](bf16x8* kf, int k0s) {
 #pragma unroll
-    for (int kk = 0; kk < QK_Q; ++kk) {
-      const int k = qq * QK_Q + kk;   // uniform
-      const int off = k < LAT_STEPS ? k_lat + k * 16
-                                    : k_rope + rope_piece(lrow, 2 * (k - LAT_STEPS) + lh) * 8;
-      kf[kk] = *reinterpret_cast<const bf16x8*>(buf + off);
+      for (int kk = 0; kk < QG; ++kk) {
+        const int k = k0s + kk;
+        const int off = k < LAT_STEPS ? k_lat + k * 16
+                                      : k_rope + rope_piece(krow, 2 * (k - LAT_STEPS) + lh) * 8;
+        kf[kk] = *reinterpret_cast<const bf16x8*>(buf + off);
+      }
+    };
+    bf16x8 kfa[QG], kfb[QG];
+    load_k(kfa, 0);
+#pragma unroll
+    for (int k0s = 0; k0s < QK_STEPS; k0s += 2 * QG) {
+      if (k0s + QG < QK_STEPS) load_k(kfb, k0s + QG);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < QG; ++kk)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfa[kk], qf[k0s + kk], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k0s + QG >= QK_STEPS) break;
+      if (k0s + 2 * QG < QK_STEPS) load_k(kfa, k0s + 2 * QG);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < QG; ++kk)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfb[kk], qf[k0s + QG + kk], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < QK_Q; ++kk)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sacc, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // hand each register quad to the wave that owns it; add the 3 others' partials
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-      xs[rh][qq][qd][lane] = f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]};
-    lds_barrier();   // the LDS writes are done before other waves pass the barrier
-    // (the own partial is read back too: indexing sacc by the wave's quarter
-    // would need register-indexed moves)
-    const f32x4 sq0 = xs[rh][0][qq][lane];
-    const f32x4 sq1 = xs[rh][1][qq][lane];
-    const f32x4 sq2 = xs[rh][2][qq][lane];
-    const f32x4 sq3 = xs[rh][3][qq][lane];
-    f32x4 sq = (sq0 + sq1) + (sq2 + sq3);
 
     // mask (only on tiles reaching past the prefix or the split end)
     if (kt + TILE > L || kt + TILE > k1) {   // uniform
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kp = kt + qkey + i;
+      for (int e = 0; e < 16; ++e) {
+        const int kp = kt + qkey + 8 * (e >> 2) + (e & 3);
         const int d = kp - L;
         const bool in_tree = d < 0 || ((anc_row >> (d & 63)) & 1ull);
-        sq[i] = (kp < k1 && in_tree) ? sq[i] : -INFINITY;
+        sacc[e] = (kp < k1 && in_tree) ? sacc[e] : -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(sq[0], sq[1]), fmaxf(sq[2], sq[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));   // this wave's keys of the row
+    float mx = sacc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));   // this wave's 32 keys of the row
     mx *= a.scale_log2;
     m_seen = fmaxf(m_seen, mx);
     if (first) {
-      // reference = the row's max over the whole tile (all 4 quads)
-      if (lh == 0) xm[rh][qq][lrow] = mx;
+      // reference = the row's max over the whole tile (both key halves)
+      if (lh == 0) xm[rh][kh][lrow] = mx;
       lds_barrier();
-      const float r4 = fmaxf(fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]),
-                             fmaxf(xm[rh][2][lrow], xm[rh][3][lrow]));
-      if (m_ref == -INFINITY) m_ref = r4;
+      const float r2 = fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]);
+      if (m_ref == -INFINITY) m_ref = r2;
+      if (empty) {
+        xp[rh][kh][0][lane] = bf16x8{};
+        xp[rh][kh][1][lane] = bf16x8{};
+        return;
+      }
     } else if (mx > m_ref + REF_SLACK) {
       restart_sh = 1u;   // all waves restart the pass with a raised reference
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    // probabilities of the quad's 4 keys: exp2(s * scale - m)
-    float p[4];
-    __bf16 pb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[i], a.scale_log2, -m_use));
-      pb[i] = (__bf16)p[i];
-    }
+    // probabilities exp2(s * scale - m); register quads 2ks, 2ks+1 form the
+    // B operand of value k-step ks of this key half
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 p01 = {pb[0], pb[1]};
-    const bf16x2 p23 = {pb[2], pb[3]};
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    lb_run = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, __builtin_amdgcn_fdot2_f32_bf16(p01, ones, lb_run, false), false);
-    xp[rh][qq][lane] = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-    lds_barrier();
-    // B operand of k-step ks: the probabilities of quads 2ks and 2ks+1
-    bf16x8 pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x2 lo = xp[rh][2 * ks][lane];
-      const u32x2 hi = xp[rh][2 * ks + 1][lane];
-      pf[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ks + i], a.scale_log2, -m_use));
+      l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      bf16x2 pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = bf16x2{(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
+        lb_run = __builtin_amdgcn_fdot2_f32_bf16(pb[i], ones, lb_run, false);
+      }
+      xp[rh][kh][ks][lane] = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, pb[0]),
+                                                              __builtin_bit_cast(uint32_t, pb[1]),
+                                                              __builtin_bit_cast(uint32_t, pb[2]),
+                                                              __builtin_bit_cast(uint32_t, pb[3])});
     }
+  };
 
-    // O^T += V^T . P^T over this wave's 128 output columns: 4 column blocks
-    // x 2 k-steps of 16 keys; V^T fragments by transpose reads
-    bf16x8 vf[O_Q][2];
+  // O^T += V^T . P^T for this wave's 256 output columns over all 64 keys of
+  // the tile: 8 column blocks x 4 k-steps of 16 keys (k-steps 0,1 from key
+  // half 0, 2,3 from key half 1); V^T fragments by transpose reads.
+  auto value_pass = [&](const uint16_t* buf) {
+    // V^T fragments of column block cb, read one block ahead of its MFMAs
+    auto load_v = [&](bf16x8* vf, int cb) {
 #pragma unroll
-    for (int cb = 0; cb < O_Q; ++cb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
         const uint16_t* p0 = buf + v_off + ks * 16 * LAT_STRIDE + cb * 32;
         const i16x4 v0 = lds_read_tr16(p0);
         const i16x4 v1 = lds_read_tr16(p0 + 8 * LAT_STRIDE);
         const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        vf[cb][ks] = __builtin_bit_cast(bf16x8, v8);
+        vf[ks] = __builtin_bit_cast(bf16x8, v8);
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    bf16x8 pf[4];
 #pragma unroll
-    for (int cb = 0; cb < O_Q; ++cb) {
-      o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][0], pf[0], o[cb], 0, 0, 0);
-      o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cb][1], pf[1], o[cb], 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) pf[ks] = xp[rh][ks >> 1][ks & 1][lane];
+    bf16x8 vfa[4], vfb[4];
+    load_v(vfa, 0);
+#pragma unroll
+    for (int cb = 0; cb < O_HALF; cb += 2) {
+      load_v(vfb, cb + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfa[ks], pf[ks], o[cb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cb + 2 < O_HALF) load_v(vfa, cb + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        o[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfb[ks], pf[ks], o[cb + 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- pipeline over the split's tiles.  Buffer u % 3 holds tile u.  Per
-  // wave the copies are issued in the order
-  //   [slots 0, 1] (wait) [tile 0, slots 2] [tile 1, slots 3] | loop t: [tile t+2, slots t+4]
-  // (slot copies on wave 4 only, rope copies on waves 0..3), and vmcnt
-  // counts them in issue order.  At the top of iteration t each wave waits
-  // until only the copies issued after its part of tile t+1 are left; wave 4
-  // also needs slots t+2, issued right after tile t, so it keeps at most
-  // tile t+1 and slots t+3 outstanding.  The barrier then publishes tile t
-  // and slots t+2 to every wave and ends all use of tile t-1, whose buffer
-  // tile t+2 overwrites.
+  // ---- pipeline over the split's tiles (two buffers; tile u in buffer u % 2).
+  // Per wave the copies are issued in the order
+  //   [slots 0, 1] (wait) [tile 0] [slots 2] | loop t: [tile t+1] [slots t+3]
+  // (slot copies on wave 0 only), and vmcnt counts them in issue order.  At
+  // the top of iteration t every wave waits for all its copies of tile t;
+  // wave 0 may keep slots t+2 (issued right after tile t) outstanding, while
+  // slots t+1, issued before tile t, have landed.  The barrier then publishes
+  // tile t and slots t+1 and ends all use of tile t-1, whose buffer tile t+1
+  // overwrites while tile t is consumed.
   uint64_t anc_row = 0ull;
   for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int c = 0; c < O_Q; ++c) {
+    for (int c = 0; c < O_HALF; ++c) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[c][e] = 0.f;
     }
@@ -511,68 +552,83 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     if (ntiles > 0) {
       issue_tile(0, tiles);
       issue_slots(2);
-      if (ntiles > 1) issue_tile(1, tiles + BUF_ELEMS);
-      issue_slots(3);
     }
 
-    int cur_buf = 0;   // tile t lives in buffer t % 3
     bool restart = false;
     for (int t = 0; t < ntiles; ++t) {
-      if (t + 1 < ntiles) {
-        if (rope_wave) vm_wait<5>(); else if (slot_wave) vm_wait<5>(); else vm_wait<4>();
-      } else {
-        if (slot_wave) vm_wait<1>(); else vm_wait<0>();
-      }
+      if (wave == 0) vm_wait<1>(); else vm_wait<0>();
       lds_barrier();   // tile t is in LDS; every wave is done with tile t-1
       if (restart_sh != 0u && pass + 1 < MAX_PASSES) {   // uniform: read after the barrier
         restart = true;
         break;
       }
-      if (t + 2 < ntiles) {
-        const int later = cur_buf == 0 ? 2 : cur_buf - 1;   // (t + 2) % 3
-        issue_tile(t + 2, tiles + later * BUF_ELEMS);
-      }
-      issue_slots(t + 4);
-      compute(t, tiles + cur_buf * BUF_ELEMS, anc_row, t == 0);
-      cur_buf = cur_buf == 2 ? 0 : cur_buf + 1;
+      if (t + 1 < ntiles) issue_tile(t + 1, tiles + ((t + 1) & 1) * BUF_ELEMS);
+      issue_slots(t + 3);
+      compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0);
+      lds_barrier();   // both key halves' probabilities are in LDS
+      value_pass(tiles + (t & 1) * BUF_ELEMS);
     }
     vm_wait<0>();
     __syncthreads();   // all copies landed and all waves are done with the tiles
     if (!restart) restart = restart_sh != 0u && pass + 1 < MAX_PASSES;
     if (!restart) break;
-    // raise the reference to the largest tile max any quarter wave has seen
-    if (lh == 0) xm[rh][qq][lrow] = m_seen;
+    // raise the reference to the largest tile max either key half has seen
+    if (lh == 0) xm[rh][kh][lrow] = m_seen;
     __syncthreads();
-    m_ref = fmaxf(fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]), fmaxf(xm[rh][2][lrow], xm[rh][3][lrow]));
+    m_ref = fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]);
     __syncthreads();
   }
 
-  // ---- store this work item's partial in the MFMA output layout: entry
-  // ((rh * 4 + qq) * O_Q + cb) * 4 + qd, lane holds float4 qd of the lane's
-  // register block cb: row rh*32 + lane%32, columns
-  // 128*qq + 32*cb + 8*qd + 4*(lane/32) .. +3 (rows past T*H are never read).
+  // ---- store the normalised partial o / lb in fp16, in the MFMA output
+  // layout: entry (rh * 16 + cb) * 4 + qd, lane holds the 4 columns qd of
+  // register block cb: row rh*32 + lane%32, columns 32*cb + 8*qd +
+  // 4*(lane/32) .. +3 (rows past T*H are never read).  Wave (rh, kh) holds
+  // blocks 8*kh .. 8*kh+7.  Each row is scaled by 2^-e so that its largest
+  // entry lies in [2^14, 2^15): any value range fits fp16, and fp16 keeps 11
+  // significant bits, finer than the bf16 output.
   {
-    f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + (int64_t)w * PART_VEC +
-                (rh * 4 + qq) * (O_Q * 4 * 64) + lane;
-#pragma unroll
-    for (int cb = 0; cb < O_Q; ++cb) {
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        po[(cb * 4 + qd) * 64] = f32x4{o[cb][4 * qd], o[cb][4 * qd + 1], o[cb][4 * qd + 2], o[cb][4 * qd + 3]};
-    }
+    // the row sums and largest |o| of the two column halves (the tile
+    // buffers are free now)
+    float* xr = reinterpret_cast<float*>(tiles);   // [rh][kh][3][32]: l, lb, max |o|
     const float l = l_run + __shfl_xor(l_run, 32);
     const float lb = lb_run + __shfl_xor(lb_run, 32);
+    float amax = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < O_HALF; ++cb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[cb][e]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (lh == 0) {
-      xl[rh][qq][0][lrow] = l;
-      xl[rh][qq][1][lrow] = lb;
+      xr[((rh * 2 + kh) * 3 + 0) * 32 + lrow] = l;
+      xr[((rh * 2 + kh) * 3 + 1) * 32 + lrow] = lb;
+      xr[((rh * 2 + kh) * 3 + 2) * 32 + lrow] = amax;
     }
     __syncthreads();
-    if (qq == 0 && lh == 0) {
-      const float lt = xl[rh][0][0][lrow] + xl[rh][1][0][lrow] + xl[rh][2][0][lrow] + xl[rh][3][0][lrow];
-      const float lbt = xl[rh][0][1][lrow] + xl[rh][1][1][lrow] + xl[rh][2][1][lrow] + xl[rh][3][1][lrow];
+    const float lt = xr[((rh * 2 + 0) * 3 + 0) * 32 + lrow] + xr[((rh * 2 + 1) * 3 + 0) * 32 + lrow];
+    const float lbt = xr[((rh * 2 + 0) * 3 + 1) * 32 + lrow] + xr[((rh * 2 + 1) * 3 + 1) * 32 + lrow];
+    const float amx = fmaxf(xr[((rh * 2 + 0) * 3 + 2) * 32 + lrow], xr[((rh * 2 + 1) * 3 + 2) * 32 + lrow]);
+    int ex = 0;
+    float scale = 0.f;   // a row without visible keys stores zeros (its weight is 0)
+    if (lbt > 0.f && amx > 0.f) {
+      ex = ilogbf(amx / lbt) - 14;
+      scale = ldexpf(1.f / lbt, -ex);
+    }
+    u32x2* po = reinterpret_cast<u32x2*>(a.part_o) + (int64_t)w * PART_VEC +
+                (rh * O_BLK + kh * O_HALF) * 4 * 64 + lane;
+#pragma unroll
+    for (int cb = 0; cb < O_HALF; ++cb) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f16x4 h = {(_Float16)(o[cb][4 * qd] * scale), (_Float16)(o[cb][4 * qd + 1] * scale),
+                         (_Float16)(o[cb][4 * qd + 2] * scale), (_Float16)(o[cb][4 * qd + 3] * scale)};
+        po[(cb * 4 + qd) * 64] = __builtin_bit_cast(u32x2, h);
+      }
+    }
+    if (kh == 0 && lh == 0) {
       const float lse2 = lt > 0.f ? m_ref + log2f(lt) : -INFINITY;
       *reinterpret_cast<float2*>(a.part_lse + ((int64_t)w * ROWS + rh * 32 + lrow) * 2) =
-          make_float2(lse2, lbt);
+          make_float2(lse2, (float)ex);
     }
   }
   st |= bad;
@@ -582,17 +638,17 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
 }
 
 // Log-sum-exp merge of the splits.  One block of 512 threads per (request,
-// row group, row half, output-column quarter, 32-column block, float4 quad):
-// 32 rows x 8 columns, read as one contiguous 1 KB piece per split.  The
-// threads first turn each split's (lse, weight sum) into the coefficient
-// exp2(lse_s - max) / lb_s of every row; then the 8 waves each accumulate an
-// eighth of the splits, 8 independent 1 KB loads at a time, and add up
-// through LDS.
+// row group, row half, 32-column block, 4-column quad):
+// 32 rows x 8 columns, read as one contiguous 512-byte piece per split.  The
+// threads first turn each split's (lse, scale exponent e) into the
+// coefficient exp2(lse_s - max) * 2^e_s of every row; then the 8 waves each
+// accumulate an eighth of the splits, 8 independent 512-byte loads at a
+// time, and add up through LDS.
 constexpr int RED_THREADS = 512;
 constexpr int RED_WAVES = RED_THREADS / 64;
 constexpr int RED_SG = RED_THREADS / 32;      // split groups of the coefficient pass
 constexpr int RED_UNROLL = 8;
-constexpr int RED_PIECES = 2 * 4 * O_Q * 4;   // blocks per row group
+constexpr int RED_PIECES = 2 * O_BLK * 4;   // blocks per row group
 
 __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   __shared__ float coef[VA_MAX_SPLITS][32];
@@ -612,10 +668,9 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
     ++r;
   }
   const int g = b / RED_PIECES;
-  const int piece = b - g * RED_PIECES;    // ((rh * 4 + qq) * O_Q + cb) * 4 + qd
-  const int rh = piece / (4 * O_Q * 4);
-  const int qq = (piece / (O_Q * 4)) & 3;
-  const int cb = (piece >> 2) % O_Q;
+  const int piece = b - g * RED_PIECES;    // (rh * 16 + cb) * 4 + qd
+  const int rh = piece / (O_BLK * 4);
+  const int cb = (piece >> 2) % O_BLK;
   const int qd = piece & 3;
   const int ns = a.nsplit[r];
   const int G = a.num_groups[r];
@@ -647,7 +702,7 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
     const float2 v = plse[(int64_t)s * G * ROWS];
     const float e = (v.x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(v.x - M);
     wsum += e;
-    coef[s][row] = (e > 0.f && v.y > 0.f) ? e / v.y : 0.f;
+    coef[s][row] = e > 0.f ? ldexpf(e, (int)v.y) : 0.f;
   }
   red_w[sg][row] = wsum;
   __syncthreads();
@@ -656,21 +711,23 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   // coefficient is 0 adds nothing, whatever its partial holds)
   const int prow = lane & 31;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o) + wbase * PART_VEC + piece * 64 + lane;
+  const u32x2* src = reinterpret_cast<const u32x2*>(a.part_o) + wbase * PART_VEC + piece * 64 + lane;
   const int64_t split_step = (int64_t)G * PART_VEC;
   for (int s0 = wave; s0 < ns; s0 += RED_WAVES * RED_UNROLL) {
-    f32x4 v[RED_UNROLL];
+    u32x2 v[RED_UNROLL];
     float c[RED_UNROLL];
 #pragma unroll
     for (int u = 0; u < RED_UNROLL; ++u) {
       const int s = s0 + u * RED_WAVES;
       const bool in = s < ns;
       c[u] = in ? coef[s][prow] : 0.f;
-      v[u] = in ? src[(int64_t)s * split_step] : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[u] = in ? src[(int64_t)s * split_step] : u32x2{0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < RED_UNROLL; ++u) {
-      if (c[u] != 0.f) acc += c[u] * v[u];
+      const f16x4 h = __builtin_bit_cast(f16x4, v[u]);
+      const f32x4 x = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      if (c[u] != 0.f) acc += c[u] * x;
     }
   }
   part[wave][lane] = acc;
@@ -704,11 +761,11 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
         lse_out = -INFINITY;
       }
       const int64_t orow = (int64_t)a.tree_begin[r] * H + rr;
-      const int col = qq * (O_Q * 32) + cb * 32 + 8 * qd + 4 * (lane >> 5);
+      const int col = cb * 32 + 8 * qd + 4 * (lane >> 5);
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[0]) | ((uint32_t)f32_to_bf16_rne(res[1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[2]) | ((uint32_t)f32_to_bf16_rne(res[3]) << 16);
       *reinterpret_cast<uint2*>(a.out + orow * DV + col) = make_uint2(lo, hi);
-      if ((piece & (4 * O_Q * 4 - 1)) == 0 && lane < 32) a.lse[orow] = lse_out;   // once per row
+      if ((piece & (O_BLK * 4 - 1)) == 0 && lane < 32) a.lse[orow] = lse_out;   // once per row
     }
   }
 }
@@ -818,7 +875,7 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
     const int64_t n = (int64_t)h_prefix_len[r] + h_num_tree[r];
     const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
     int64_t ns = forced > 0 ? forced : (n + keys_per_item - 1) / keys_per_item;
-    const int64_t max_ns = (n + TILE - 1) / TILE;
+    const int64_t max_ns = (n + SPLIT_ALIGN - 1) / SPLIT_ALIGN;
     if (ns > max_ns) ns = max_ns;
     if (ns > VA_MAX_SPLITS) ns = VA_MAX_SPLITS;
     if (ns < 1) ns = 1;
@@ -835,7 +892,7 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
   p.total_work = (int32_t)work;
   p.total_tree = (int32_t)tree;
   p.total_rows = (int32_t)(tree * num_heads);
-  const int64_t o_bytes = align256(work * ROWS * DV * (int64_t)sizeof(float));
+  const int64_t o_bytes = align256(work * ROWS * DV * (int64_t)sizeof(uint16_t));
   const int64_t lse_bytes = align256(work * ROWS * 2 * (int64_t)sizeof(float));
   const int64_t st_bytes = align256(work * (int64_t)sizeof(uint32_t));
   p.lse_offset = o_bytes;
@@ -879,7 +936,7 @@ int verify_attn_run(const va_plan* plan, const uint16_t* q, const uint16_t* kv_p
   a.prefix_len = prefix_len;
   a.parent = parent;
   char* ws = static_cast<char*>(workspace);
-  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_o = reinterpret_cast<uint32_t*>(ws);
   a.part_lse = reinterpret_cast<float*>(ws + plan->lse_offset);
   a.status = reinterpret_cast<uint32_t*>(ws + plan->status_offset);
   for (int r = 0; r < plan->num_requests; ++r) {
@@ -907,7 +964,7 @@ int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out
   ReduceArgs a;
   std::memset(&a, 0, sizeof a);
   const char* ws = static_cast<const char*>(workspace);
-  a.part_o = reinterpret_cast<const float*>(ws);
+  a.part_o = reinterpret_cast<const uint32_t*>(ws);
   a.part_lse = reinterpret_cast<const float*>(ws + plan->lse_offset);
   a.status = reinterpret_cast<const uint32_t*>(ws + plan->status_offset);
   a.out = out;

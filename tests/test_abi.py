@@ -51,13 +51,13 @@ def _plan(H, L, T, cus=256):
 
 def test_plan_long_prefix_h8_t16():
     p = _plan(8, [65536], [16])
-    assert p.magic == binding.VA_PLAN_MAGIC and p.rows_per_group == 64 and p.tile_keys == 32
+    assert p.magic == binding.VA_PLAN_MAGIC and p.rows_per_group == 64 and p.tile_keys == 64
     assert p.num_groups[0] == 2                     # 128 rows / 64
     # keys x groups spread over 256 CUs: 2 * 65552 / 256 = 512 keys per work item
     assert p.nsplit[0] == 128
     assert p.total_work == 256
     assert p.total_tree == 16 and p.total_rows == 128
-    o = 256 * 64 * 512 * 4
+    o = 256 * 64 * 512 * 2                          # fp16 partial outputs
     assert p.lse_offset == o
     assert p.status_offset == o + 256 * 64 * 8
     assert p.workspace_bytes == o + 256 * 64 * 8 + 1024
