@@ -20,6 +20,10 @@ HIPCC_FLAGS = [
     "-fPIC",
     # keep hipcc from forming packed fp32 instructions on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in arch VGPRs: the partial kernel keeps Q (144 registers)
+    # as an MFMA operand in AGPRs and its output accumulators in VGPRs; the
+    # AGPR-result form makes the allocator copy the accumulators every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

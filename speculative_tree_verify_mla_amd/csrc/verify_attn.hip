@@ -333,30 +333,47 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
       dma4_v(lds_addr(&sring[u & (SLOT_RING - 1)][0]), table + k);
     }
   };
-  auto issue_tile = [&](int u, uint16_t* buf) {
-    const int32_t vslot = sring[u & (SLOT_RING - 1)][lane];
+  // The copies of a tile are issued in ISSUE_PARTS pieces spread over the
+  // score MFMAs of the previous tile: a burst of all of them stalls the wave
+  // on memory back-pressure while the MFMA pipe idles.
+  struct TileIssue {
+    int32_t vslot;   // slot of key `lane` of the tile
+    uint64_t use;    // bit j: key j is read (exists and its slot is in the pool)
+    uint32_t lbuf;   // LDS byte address of the tile buffer
+  };
+  auto prepare_tile = [&](int u, uint16_t* buf) -> TileIssue {
+    TileIssue ti;
+    ti.vslot = sring[u & (SLOT_RING - 1)][lane];
     const int k = k0 + u * TILE + lane;
     const bool exists = k < k1;
-    const bool inside = vslot >= 0 && (int64_t)vslot < a.num_slots;
+    const bool inside = ti.vslot >= 0 && (int64_t)ti.vslot < a.num_slots;
     if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
-    const uint64_t use = __ballot(exists && inside);   // bit j: key j of the tile is read
-    const uint32_t lbuf = lds_addr(buf);
+    ti.use = __ballot(exists && inside);
+    ti.lbuf = lds_addr(buf);
+    return ti;
+  };
+  // copies 2*part, 2*part+1 of the tile: 0..15 latent rows, 16..17 rope blocks
+  auto issue_part = [&](const TileIssue& ti, int part) {
 #pragma unroll
-    for (int j = 0; j < LAT_DMA; ++j) {
-      const int key = wave * LAT_DMA + j;
-      const int32_t sj = __builtin_amdgcn_readlane(vslot, key);
-      const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sj * a.stride : va_zero_row;
-      dma16_s(lbuf + key * (LAT_STRIDE * 2), row, lane * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < ROPE_DMA; ++j) {
-      const int kb = (wave * ROPE_DMA + j) * 8;   // first key of this rope block
-      const int key = kb + (lane >> 3);          // key of this lane
-      const int32_t sk = __shfl(vslot, key);
-      const uint16_t* row = ((use >> key) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
-      dma16_v(lbuf + (LAT_ELEMS + kb * DROPE) * 2, row + DV + rope_piece(key, lane & 7) * 8);
+    for (int c = 2 * part; c < 2 * part + 2; ++c) {
+      if (c < LAT_DMA) {
+        const int key = wave * LAT_DMA + c;
+        const int32_t sj = __builtin_amdgcn_readlane(ti.vslot, key);
+        const uint64_t ok = 0ull - ((ti.use >> key) & 1ull);   // all ones when the row is read
+        const uint64_t row = ((uint64_t)(a.kv + (int64_t)sj * a.stride) & ok) |
+                             ((uint64_t)va_zero_row & ~ok);
+        dma16_s(ti.lbuf + key * (LAT_STRIDE * 2), (const void*)row, lane * 16);
+      } else {
+        const int kb = (wave * ROPE_DMA + (c - LAT_DMA)) * 8;   // first key of this rope block
+        const int key = kb + (lane >> 3);                        // key of this lane
+        const int32_t sk = __shfl(ti.vslot, key);
+        const uint16_t* row = ((ti.use >> key) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
+        dma16_v(ti.lbuf + (LAT_ELEMS + kb * DROPE) * 2, row + DV + rope_piece(key, lane & 7) * 8);
+      }
     }
   };
+  static_assert(LAT_DMA + ROPE_DMA == 2 * 9, "copies of a tile = 2 per score MFMA group");
+
 
   f32x16 o[O_HALF];
   // The reference this row's probabilities are taken against (common to the
@@ -384,23 +401,16 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
 
   // Consumes tile t (one buffer).  `first` is set on the first tile of a
   // pass: the two key-half waves then agree on each row's reference.
-  auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row, bool first) {
+  auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row, bool first,
+                     const TileIssue& nxt) {
     const int kt = k0 + t * TILE;
-    // a key half lying wholly past the split end contributes zero weights
-    // (uniform; the first tile still joins the reference exchange)
-    const bool empty = kt + kh * HALF >= k1;
-    if (empty && !first) {
-      xp[rh][kh][0][lane] = bf16x8{};
-      xp[rh][kh][1][lane] = bf16x8{};
-      return;
-    }
     // S^T = K . Q^T for this wave's 32 keys over all 576 score columns
     f32x16 sacc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
     // K fragments in groups of QG k-steps, the next group's LDS reads issued
     // ahead of the current group's MFMAs
-    constexpr int QG = 6;
+    constexpr int QG = 4;
     auto load_k = [&](bf16x8* kf, int k0s) {
 #pragma unroll
       for (int kk = 0; kk < QG; ++kk) {
@@ -410,22 +420,19 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
         kf[kk] = *reinterpret_cast<const bf16x8*>(buf + off);
       }
     };
+    // after each group's MFMAs, 2 of the next tile's copies
     bf16x8 kfa[QG], kfb[QG];
     load_k(kfa, 0);
 #pragma unroll
-    for (int k0s = 0; k0s < QK_STEPS; k0s += 2 * QG) {
-      if (k0s + QG < QK_STEPS) load_k(kfb, k0s + QG);
+    for (int g = 0; g < QK_STEPS / QG; ++g) {
+      bf16x8* cur = (g & 1) ? kfb : kfa;
+      bf16x8* ahead = (g & 1) ? kfa : kfb;
+      if (g + 1 < QK_STEPS / QG) load_k(ahead, (g + 1) * QG);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < QG; ++kk)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfa[kk], qf[k0s + kk], sacc, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k0s + QG >= QK_STEPS) break;
-      if (k0s + 2 * QG < QK_STEPS) load_k(kfa, k0s + 2 * QG);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < QG; ++kk)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfb[kk], qf[k0s + QG + kk], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[kk], qf[g * QG + kk], sacc, 0, 0, 0);
+      issue_part(nxt, g);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -451,11 +458,6 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
       lds_barrier();
       const float r2 = fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]);
       if (m_ref == -INFINITY) m_ref = r2;
-      if (empty) {
-        xp[rh][kh][0][lane] = bf16x8{};
-        xp[rh][kh][1][lane] = bf16x8{};
-        return;
-      }
     } else if (mx > m_ref + REF_SLACK) {
       restart_sh = 1u;   // all waves restart the pass with a raised reference
     }
@@ -523,13 +525,12 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
 
   // ---- pipeline over the split's tiles (two buffers; tile u in buffer u % 2).
   // Per wave the copies are issued in the order
-  //   [slots 0, 1] (wait) [tile 0] [slots 2] | loop t: [tile t+1] [slots t+3]
-  // (slot copies on wave 0 only), and vmcnt counts them in issue order.  At
-  // the top of iteration t every wave waits for all its copies of tile t;
-  // wave 0 may keep slots t+2 (issued right after tile t) outstanding, while
-  // slots t+1, issued before tile t, have landed.  The barrier then publishes
-  // tile t and slots t+1 and ends all use of tile t-1, whose buffer tile t+1
-  // overwrites while tile t is consumed.
+  //   [slots 0, 1] (wait) [tile 0] [slots 2] | loop t: [slots t+3] [tile t+1]
+  // (slot copies on wave 0 only; the copies of tile t+1 are spread over the
+  // score MFMAs of tile t).  At the top of iteration t every wave waits for
+  // all its copies, which are those of tile t and the slots up to t+2.  The
+  // barrier then publishes tile t and slots t+1 and ends all use of tile
+  // t-1, whose buffer tile t+1 overwrites while tile t is consumed.
   uint64_t anc_row = 0ull;
   for (int pass = 0;; ++pass) {
 #pragma unroll
@@ -550,21 +551,25 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     __syncthreads();   // slots 0, 1, anc[], status_sh and restart_sh ready
     if (pass == 0) anc_row = row_ok ? anc[rho / H] : 0ull;
     if (ntiles > 0) {
-      issue_tile(0, tiles);
+      const TileIssue first_tile = prepare_tile(0, tiles);
+#pragma unroll
+      for (int g = 0; g < 9; ++g) issue_part(first_tile, g);
       issue_slots(2);
     }
 
     bool restart = false;
     for (int t = 0; t < ntiles; ++t) {
-      if (wave == 0) vm_wait<1>(); else vm_wait<0>();
+      vm_wait<0>();
       lds_barrier();   // tile t is in LDS; every wave is done with tile t-1
       if (restart_sh != 0u && pass + 1 < MAX_PASSES) {   // uniform: read after the barrier
         restart = true;
         break;
       }
-      if (t + 1 < ntiles) issue_tile(t + 1, tiles + ((t + 1) & 1) * BUF_ELEMS);
+      // the next tile's copies; after the last tile they copy the zero row
+      // (every key lies past the split end) into the free buffer
+      const TileIssue nxt = prepare_tile(t + 1, tiles + ((t + 1) & 1) * BUF_ELEMS);
       issue_slots(t + 3);
-      compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0);
+      compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0, nxt);
       lds_barrier();   // both key halves' probabilities are in LDS
       value_pass(tiles + (t & 1) * BUF_ELEMS);
     }
