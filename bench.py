@@ -119,34 +119,40 @@ def main():
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
 
-    def step(i, reduce=True, pool_set=None):
-        ps = pools if pool_set is None else pool_set
-        va.verify_attn_run(plan, q, ps[i % len(ps)], table, indptr, prefix, parent, wl.sm_scale,
-                           ws, stream)
-        if reduce:
-            va.verify_attn_reduce(plan, ws, out, lse, stream)
+    # split-verify decomposition of the same call (prefix kernel + tree-block
+    # kernel + the same reduce), timed beside the fused kernel
+    plan_split = va.verify_attn_plan(H, wl.prefix_len, wl.num_tree, split_tree=True)
+    ws_split = va.workspace_for(plan_split, dev)
 
-    def capture(n, reduce=True, pool_set=None):
+    def step(i, reduce=True, pool_set=None, split=False):
+        ps = pools if pool_set is None else pool_set
+        pl, w = (plan_split, ws_split) if split else (plan, ws)
+        va.verify_attn_run(pl, q, ps[i % len(ps)], table, indptr, prefix, parent, wl.sm_scale,
+                           w, stream)
+        if reduce:
+            va.verify_attn_reduce(pl, w, out, lse, stream)
+
+    def capture(n, reduce=True, pool_set=None, split=False):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             with torch.cuda.graph(g, stream=stream):
                 for i in range(n):
-                    step(i, reduce, pool_set)
+                    step(i, reduce, pool_set, split)
         return g
 
-    def timed(n, reduce=True, pool_set=None):
+    def timed(n, reduce=True, pool_set=None, split=False):
         """Run n steps between two syncs; return (ms from HIP events recorded on
         `stream` around the steps, host wall seconds between the syncs)."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        g = None if args.eager else capture(n, reduce, pool_set)
+        g = None if args.eager else capture(n, reduce, pool_set, split)
         torch.cuda.synchronize()
         w0 = time.time()
         with torch.cuda.stream(stream):
             e0.record(stream)
             if g is None:
                 for i in range(n):
-                    step(i, reduce, pool_set)
+                    step(i, reduce, pool_set, split)
             else:
                 g.replay()
             e1.record(stream)
@@ -170,6 +176,11 @@ def main():
     ms_partial = timed(K, reduce=False)[0] / K
     ms_warm = timed(K, pool_set=[pools[0]])[0] / K
     ms_partial_warm = timed(K, reduce=False, pool_set=[pools[0]])[0] / K
+    ms_split = timed(K, split=True)[0] / K
+    out_split = out.clone()
+    step(0)
+    torch.cuda.synchronize()
+    split_vs_fused = float((out_split.float() - out.float()).abs().max())
     print(f"# timed {K} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
     kv_bytes = wl.kv_bytes()
@@ -268,6 +279,13 @@ def main():
             "traffic": traffic,
             "avg_us": round(ms_partial * 1e3, 3),
             "warm_avg_us": round(ms_partial_warm * 1e3, 3),
+        },
+        "ab_split_verify": {
+            "mode": "prefix kernel without tree mask + tree-block kernel + the same reduce",
+            "us_per_call": round(ms_split * 1e3, 3),
+            "value": round(kv_bytes / (ms_split * 1e-3) / 1e9, 2),
+            "nsplit": plan_split.splits(),
+            "max_abs_out_vs_fused": split_vs_fused,
         },
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

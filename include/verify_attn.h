@@ -96,6 +96,8 @@ typedef struct va_plan {
   int32_t total_tree;        /* sum of T_r */
   int32_t total_rows;        /* sum of T_r * H */
   int32_t num_cus;           /* compute units the plan was sized for */
+  int32_t mode;              /* VA_MODE_FUSED or VA_MODE_SPLIT_TREE */
+  int32_t reserved;          /* zero */
   int64_t workspace_bytes;   /* bytes verify_attn_run needs */
   int64_t lse_offset;        /* byte offset of the partial-lse region */
   int64_t status_offset;     /* byte offset of the per-work-item status words */
@@ -108,7 +110,23 @@ typedef struct va_plan {
 } va_plan;
 
 #define VA_PLAN_MAGIC 0x56415054u /* "VAPT" */
-#define VA_PLAN_VERSION 1u
+#define VA_PLAN_VERSION 2u
+
+/* How verify_attn_run decomposes the keys of a request (va_plan.mode).
+ * VA_MODE_FUSED: one partial kernel; its splits cover slices of all L + T
+ *   keys, and the tiles that reach into the draft block apply the tree mask.
+ * VA_MODE_SPLIT_TREE: the split-verify decomposition ("The Architecture
+ *   Detective", section "The Split Verify Design": the draft queries attend
+ *   the prefix densely, only the small tree block needs the custom mask, and
+ *   a log-sum-exp merge joins the two).  A prefix kernel without any tree
+ *   mask covers the L prefix keys in nsplit-1 splits, and a tree-block
+ *   kernel covers the T draft keys as split nsplit-1.  The same reduce merges
+ *   both.  Results agree with the fused mode to rounding. */
+#define VA_MODE_FUSED 0
+#define VA_MODE_SPLIT_TREE 1
+
+/* verify_attn_plan_ex flags */
+#define VA_PLAN_SPLIT_TREE 1u   /* plan VA_MODE_SPLIT_TREE instead of VA_MODE_FUSED */
 
 /*
  * verify_attn_plan - size the split-KV schedule and the workspace (host only).
@@ -130,12 +148,24 @@ typedef struct va_plan {
  * raised it from 16 to 64 for occupancy) is chosen from the compute-unit
  * count, the rows T_r*H and the key counts so that every work item gets a
  * similar number of keys.  The environment variable VA_NSPLIT, read here
- * only, forces one split count for every request (for tuning sweeps).
+ * only, forces one split count for every request (for tuning sweeps; with
+ * VA_PLAN_SPLIT_TREE it is the count of prefix splits).
  * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_HIP (device query failed).
  */
 int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
                      const int32_t* h_num_tree, int32_t num_cus, va_plan* plan,
                      size_t* workspace_bytes);
+
+/*
+ * verify_attn_plan_ex - verify_attn_plan with flags.  flags = 0 is
+ * verify_attn_plan (VA_MODE_FUSED); VA_PLAN_SPLIT_TREE plans the
+ * split-verify decomposition (VA_MODE_SPLIT_TREE): nsplit[r] counts the
+ * prefix splits plus the one tree-block split.  Unknown flag bits are
+ * VA_ERR_SHAPE.  Other arguments and errors as verify_attn_plan.
+ */
+int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
+                        const int32_t* h_num_tree, int32_t num_cus, uint32_t flags,
+                        va_plan* plan, size_t* workspace_bytes);
 
 /*
  * verify_attn_run - partial pass (enqueue only).

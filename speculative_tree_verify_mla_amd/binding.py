@@ -23,6 +23,10 @@ VA_MAX_TREE = 64
 VA_MAX_REQUESTS = 64
 VA_MAX_SPLITS = 256
 VA_PLAN_MAGIC = 0x56415054
+VA_PLAN_VERSION = 2
+VA_MODE_FUSED = 0
+VA_MODE_SPLIT_TREE = 1
+VA_PLAN_SPLIT_TREE = 1
 
 VA_OK = 0
 ERRORS = {
@@ -33,7 +37,8 @@ STATUS_BITS = {1: "BAD_PREFIX", 2: "SHORT_TABLE", 4: "BAD_SLOT", 8: "BAD_PARENT"
 
 # Every symbol include/verify_attn.h declares.
 EXPORTS = (
-    "verify_attn_plan", "verify_attn_run", "verify_attn_reduce", "verify_attn_read_status",
+    "verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
+    "verify_attn_read_status",
     "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_error_string",
     "verify_attn_plan_struct_size",
 )
@@ -47,6 +52,7 @@ class VaPlan(ctypes.Structure):
         ("rows_per_group", ctypes.c_int32), ("tile_keys", ctypes.c_int32),
         ("total_work", ctypes.c_int32), ("total_tree", ctypes.c_int32),
         ("total_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+        ("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64), ("lse_offset", ctypes.c_int64),
         ("status_offset", ctypes.c_int64),
         ("num_tree", ctypes.c_int32 * VA_MAX_REQUESTS),
@@ -83,6 +89,8 @@ def load_library(path: os.PathLike | None = None):
     i32, i64, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.verify_attn_plan.argtypes = [i32, i32, P, P, i32, ctypes.POINTER(VaPlan),
                                      ctypes.POINTER(sz)]
+    lib.verify_attn_plan_ex.argtypes = [i32, i32, P, P, i32, ctypes.c_uint32,
+                                        ctypes.POINTER(VaPlan), ctypes.POINTER(sz)]
     lib.verify_attn_run.argtypes = [ctypes.POINTER(VaPlan), P, P, i64, i32, P, i32, P, P, P, f32,
                                     P, sz, P]
     lib.verify_attn_reduce.argtypes = [ctypes.POINTER(VaPlan), P, P, P, P]
@@ -94,7 +102,7 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_error_string.restype = ctypes.c_char_p
     lib.verify_attn_plan_struct_size.argtypes = []
     lib.verify_attn_plan_struct_size.restype = sz
-    for name in ("verify_attn_plan", "verify_attn_run", "verify_attn_reduce",
+    for name in ("verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
                  "verify_attn_read_status", "verify_attn_check_tree", "verify_attn_gather_rows"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.verify_attn_plan_struct_size() != ctypes.sizeof(VaPlan):
@@ -138,18 +146,25 @@ def _bf16_types():
 
 
 # --------------------------------------------------------------------------- C ABI mirrors
-def verify_attn_plan(num_heads, prefix_len, num_tree, num_cus=0) -> VaPlan:
-    """Host-only plan.  prefix_len / num_tree: per-request host sequences."""
+def verify_attn_plan(num_heads, prefix_len, num_tree, num_cus=0, split_tree=False) -> VaPlan:
+    """Host-only plan.  prefix_len / num_tree: per-request host sequences.
+    split_tree=True plans the split-verify decomposition (verify_attn_plan_ex
+    with VA_PLAN_SPLIT_TREE); otherwise verify_attn_plan."""
     pl = _i32_host(prefix_len)
     nt = _i32_host(num_tree)
     if pl.shape != nt.shape:
         raise ValueError("prefix_len and num_tree must have one entry per request")
     plan = VaPlan()
     ws = ctypes.c_size_t(0)
-    rc = load_library().verify_attn_plan(
-        int(nt.shape[0]), int(num_heads), pl.ctypes.data_as(ctypes.c_void_p),
-        nt.ctypes.data_as(ctypes.c_void_p), int(num_cus), ctypes.byref(plan), ctypes.byref(ws))
-    _check("verify_attn_plan", rc)
+    args = (int(nt.shape[0]), int(num_heads), pl.ctypes.data_as(ctypes.c_void_p),
+            nt.ctypes.data_as(ctypes.c_void_p), int(num_cus))
+    lib = load_library()
+    if split_tree:
+        rc = lib.verify_attn_plan_ex(*args, VA_PLAN_SPLIT_TREE, ctypes.byref(plan), ctypes.byref(ws))
+        _check("verify_attn_plan_ex", rc)
+    else:
+        rc = lib.verify_attn_plan(*args, ctypes.byref(plan), ctypes.byref(ws))
+        _check("verify_attn_plan", rc)
     return plan
 
 
@@ -235,7 +250,7 @@ def workspace_for(plan, device="cuda"):
 
 def verify_attn(q, kv_pool, slot_table, slot_indptr, prefix_len, parent, sm_scale, *,
                 num_tree, prefix_len_host, plan=None, workspace=None, out=None, lse=None,
-                stream=None):
+                stream=None, split_tree=False):
     """plan (if not given) + run + reduce.  Returns (out [sumT,H,512] bf16, lse [sumT,H] fp32).
 
     num_tree / prefix_len_host: host sequences per request (prefix_len_host is
@@ -243,7 +258,7 @@ def verify_attn(q, kv_pool, slot_table, slot_indptr, prefix_len, parent, sm_scal
     import torch
     H = int(q.shape[1])
     if plan is None:
-        plan = verify_attn_plan(H, prefix_len_host, num_tree)
+        plan = verify_attn_plan(H, prefix_len_host, num_tree, split_tree=split_tree)
     if workspace is None:
         workspace = workspace_for(plan, q.device)
     total_tree = int(plan.total_tree)

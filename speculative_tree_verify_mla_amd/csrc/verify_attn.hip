@@ -224,17 +224,59 @@ __device__ __forceinline__ int32_t table_entry(const int32_t* __restrict__ table
 // LDS banks for the score MFMA reads.
 __device__ __forceinline__ int rope_piece(int key, int piece) { return piece ^ ((key >> 1) & 7); }
 
-__global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2 * BUF_ELEMS];
+// Which keys a launch of the partial kernel covers.
+//   FUSED:  every split of a request covers a slice of its L + T keys; tiles
+//           reaching into the draft block apply the tree mask.
+//   PREFIX: splits 0 .. ns-2 cover slices of the L prefix keys only, with no
+//           tree mask; split ns-1 (the tree block) is left to TREE.
+//   TREE:   one work item per (request, row group): the T draft keys, with
+//           the tree mask.
+// PREFIX + TREE is the split-verify decomposition ("The Architecture
+// Detective", section "The Split Verify Design": a dense prefix pass and a
+// small masked tree-block pass joined by the log-sum-exp merge); the reduce
+// is the same for both.
+enum KernelMode { FUSED = 0, PREFIX = 1, TREE = 2 };
+
+// LDS of one work item (163,344 bytes of the 160 KB).
+struct PartialSmem {
+  __attribute__((aligned(16))) uint16_t tiles[2 * BUF_ELEMS];
   // bf16 probabilities [row half][key half][lane] (two value-MFMA operands per
   // lane); before the first tile the same bytes hold the ancestor masks
-  __shared__ __attribute__((aligned(16))) bf16x8 xp[2][2][2][64];
-  __shared__ int32_t sring[SLOT_RING][TILE];   // slot-table entries of upcoming tiles
-  __shared__ float xm[2][2][32];               // per-row maxima [row half][key half][row]
-  __shared__ uint32_t status_sh;
-  __shared__ uint32_t restart_sh;
+  __attribute__((aligned(16))) bf16x8 xp[2][2][2][64];
+  int32_t sring[SLOT_RING][TILE];   // slot-table entries of upcoming tiles
+  float xm[2][2][32];               // per-row maxima [row half][key half][row]
+  uint32_t status_sh;
+  uint32_t restart_sh;
+};
+static_assert(sizeof(PartialSmem::xp) >= VA_MAX_TREE * sizeof(uint64_t), "ancestor masks fit");
+
+template <int MODE>
+__device__ __forceinline__ void partial_body(const PartialArgs& a, int block, PartialSmem& sm);
+
+// FUSED launch: one block per work item (XCD-ordered, see partial_body).
+__global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
+  __shared__ PartialSmem sm;
+  partial_body<FUSED>(a, blockIdx.x, sm);
+}
+
+// SPLIT_TREE launch: the tree-block work items (blocks 0 .. tree_blocks-1)
+// and the prefix work items share one grid, so the small tree block runs on
+// its own compute units alongside the prefix splits instead of before them.
+__global__ __launch_bounds__(THREADS, 1) void va_split_kernel(PartialArgs a, int tree_blocks) {
+  __shared__ PartialSmem sm;
+  if ((int)blockIdx.x < tree_blocks) partial_body<TREE>(a, blockIdx.x, sm);
+  else partial_body<PREFIX>(a, blockIdx.x - tree_blocks, sm);
+}
+
+template <int MODE>
+__device__ __forceinline__ void partial_body(const PartialArgs& a, int block, PartialSmem& sm) {
+  uint16_t* const tiles = sm.tiles;
+  bf16x8 (&xp)[2][2][2][64] = sm.xp;
+  int32_t (&sring)[SLOT_RING][TILE] = sm.sring;
+  float (&xm)[2][2][32] = sm.xm;
+  uint32_t& status_sh = sm.status_sh;
+  uint32_t& restart_sh = sm.restart_sh;
   uint64_t* anc = reinterpret_cast<uint64_t*>(&xp[0][0][0][0]);   // [VA_MAX_TREE]
-  static_assert(sizeof(xp) >= VA_MAX_TREE * sizeof(uint64_t), "ancestor masks fit");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -247,17 +289,28 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
   // Work items are ordered (request, split, row group); block b runs on XCD
   // b % 8, so each XCD takes a contiguous run of work items and the row
   // groups that read the same KV split share that XCD's L2.
-  const int per_xcd = (a.total_work + 7) >> 3;
-  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (w >= a.total_work) return;
-
-  int r = 0;
-  while (r + 1 < a.num_requests && a.work_begin[r + 1] <= w) ++r;
+  int w, r = 0;
+  if (MODE == TREE) {
+    // block b -> (request, row group) of the tree-block work items
+    int b = block;
+    while (r + 1 < a.num_requests && b >= a.num_groups[r]) {
+      b -= a.num_groups[r];
+      ++r;
+    }
+    if (b >= a.num_groups[r]) return;
+    w = a.work_begin[r] + (a.nsplit[r] - 1) * a.num_groups[r] + b;
+  } else {
+    const int per_xcd = (a.total_work + 7) >> 3;
+    w = (block & 7) * per_xcd + (block >> 3);
+    if (w >= a.total_work) return;
+    while (r + 1 < a.num_requests && a.work_begin[r + 1] <= w) ++r;
+  }
   const int G = a.num_groups[r];
   const int local = w - a.work_begin[r];
   const int s = local / G;
   const int g = local - s * G;
   const int ns = a.nsplit[r];
+  if (MODE == PREFIX && s == ns - 1) return;   // the tree block
   const int T = a.num_tree[r];
   const int H = a.num_heads;
   const int rows_r = T * H;
@@ -279,14 +332,25 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     n_valid = (tab0 < 0 || tab1 < tab0 || tab0 >= a.slot_table_len)
                   ? 0 : min(min(tab1, a.slot_table_len) - tab0, n);
   }
-  const int chunk = ((n + ns - 1) / ns + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
-  const int k0 = s * chunk;
-  const int k1 = min(n_valid, k0 + chunk);   // end of this split (keys past a short table dropped)
+  int k0, k1;   // key range of this split (keys past a short table dropped)
+  if (MODE == FUSED) {
+    const int chunk = ((n + ns - 1) / ns + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
+    k0 = s * chunk;
+    k1 = min(n_valid, k0 + chunk);
+  } else if (MODE == PREFIX) {
+    const int np = ns - 1;   // >= 1 here
+    const int chunk = ((L + np - 1) / np + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
+    k0 = min(s * chunk, L);
+    k1 = min(min(n_valid, L), k0 + chunk);
+  } else {
+    k0 = L;
+    k1 = min(n_valid, n);
+  }
   const int ntiles = k1 > k0 ? (k1 - k0 + TILE - 1) / TILE : 0;
   const int32_t* table = a.slot_table + (n_valid > 0 ? tab0 : 0);
 
   // ---- ancestor masks (bit j of anc[i]: draft node j is i or an ancestor of i)
-  if (tid < VA_MAX_TREE) {
+  if (MODE != PREFIX && tid < VA_MAX_TREE) {
     uint64_t m = 0;
     if (tid < T) {
       const int32_t* par = a.parent + a.tree_begin[r];
@@ -437,12 +501,12 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     }
 
     // mask (only on tiles reaching past the prefix or the split end)
-    if (kt + TILE > L || kt + TILE > k1) {   // uniform
+    if (MODE == PREFIX ? kt + TILE > k1 : (kt + TILE > L || kt + TILE > k1)) {   // uniform
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kp = kt + qkey + 8 * (e >> 2) + (e & 3);
         const int d = kp - L;
-        const bool in_tree = d < 0 || ((anc_row >> (d & 63)) & 1ull);
+        const bool in_tree = MODE == PREFIX || d < 0 || ((anc_row >> (d & 63)) & 1ull);
         sacc[e] = (kp < k1 && in_tree) ? sacc[e] : -INFINITY;
       }
     }
@@ -549,7 +613,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
     // no wait of its own before their first use
     wait_vmcnt<0>();
     __syncthreads();   // slots 0, 1, anc[], status_sh and restart_sh ready
-    if (pass == 0) anc_row = row_ok ? anc[rho / H] : 0ull;
+    if (pass == 0 && MODE != PREFIX) anc_row = row_ok ? anc[rho / H] : 0ull;
     if (ntiles > 0) {
       const TileIssue first_tile = prepare_tile(0, tiles);
 #pragma unroll
@@ -827,9 +891,16 @@ int query_num_cus(int32_t* out) {
 }
 
 bool plan_ok(const va_plan* p) {
-  return p != nullptr && p->magic == VA_PLAN_MAGIC && p->version == VA_PLAN_VERSION &&
-         p->num_requests >= 1 && p->num_requests <= VA_MAX_REQUESTS && p->total_work >= 1 &&
-         p->rows_per_group == ROWS && p->tile_keys == TILE;
+  if (p == nullptr || p->magic != VA_PLAN_MAGIC || p->version != VA_PLAN_VERSION ||
+      p->num_requests < 1 || p->num_requests > VA_MAX_REQUESTS || p->total_work < 1 ||
+      p->rows_per_group != ROWS || p->tile_keys != TILE ||
+      (p->mode != VA_MODE_FUSED && p->mode != VA_MODE_SPLIT_TREE))
+    return false;
+  if (p->mode == VA_MODE_SPLIT_TREE) {
+    for (int r = 0; r < p->num_requests; ++r)
+      if (p->nsplit[r] < 2) return false;   // at least one prefix split + the tree block
+  }
+  return true;
 }
 
 }  // namespace
@@ -839,7 +910,16 @@ extern "C" {
 int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
                      const int32_t* h_num_tree, int32_t num_cus, va_plan* plan,
                      size_t* workspace_bytes) {
+  return verify_attn_plan_ex(num_requests, num_heads, h_prefix_len, h_num_tree, num_cus, 0u, plan,
+                             workspace_bytes);
+}
+
+int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
+                        const int32_t* h_num_tree, int32_t num_cus, uint32_t flags,
+                        va_plan* plan, size_t* workspace_bytes) {
   if (h_prefix_len == nullptr || h_num_tree == nullptr || plan == nullptr) return VA_ERR_NULL;
+  if ((flags & ~VA_PLAN_SPLIT_TREE) != 0u) return VA_ERR_SHAPE;
+  const bool split_tree = (flags & VA_PLAN_SPLIT_TREE) != 0u;
   if (num_requests < 1 || num_requests > VA_MAX_REQUESTS) return VA_ERR_SHAPE;
   if (num_heads < 1 || num_heads > VA_MAX_HEADS) return VA_ERR_SHAPE;
   if (num_cus < 0) return VA_ERR_SHAPE;
@@ -860,14 +940,20 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
   p.rows_per_group = ROWS;
   p.tile_keys = TILE;
   p.num_cus = num_cus;
+  p.mode = split_tree ? VA_MODE_SPLIT_TREE : VA_MODE_FUSED;
 
-  // Split count: balance keys x row groups over the compute units.
+  // Split count: balance keys x row groups over the compute units (in the
+  // split-tree mode over the prefix keys only; the tree block is one more
+  // split per request, run by its own small kernel).
   int64_t units = 0;
+  int64_t cus = num_cus;
   for (int r = 0; r < num_requests; ++r) {
     const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
-    units += groups * ((int64_t)h_prefix_len[r] + h_num_tree[r]);
+    units += groups * ((int64_t)h_prefix_len[r] + (split_tree ? 0 : h_num_tree[r]));
+    if (split_tree) cus -= groups;   // compute units the tree-block work items occupy
   }
-  int64_t keys_per_item = (units + num_cus - 1) / num_cus;
+  if (cus < 1) cus = 1;
+  int64_t keys_per_item = (units + cus - 1) / cus;
   if (keys_per_item < MIN_KEYS_PER_SPLIT) keys_per_item = MIN_KEYS_PER_SPLIT;
   int forced = 0;
   if (const char* e = std::getenv("VA_NSPLIT")) forced = std::atoi(e);
@@ -877,13 +963,16 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
   p.tree_begin[0] = 0;
   p.work_begin[0] = 0;
   for (int r = 0; r < num_requests; ++r) {
-    const int64_t n = (int64_t)h_prefix_len[r] + h_num_tree[r];
+    // keys the (prefix) splits share
+    const int64_t n = (int64_t)h_prefix_len[r] + (split_tree ? 0 : h_num_tree[r]);
     const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
     int64_t ns = forced > 0 ? forced : (n + keys_per_item - 1) / keys_per_item;
     const int64_t max_ns = (n + SPLIT_ALIGN - 1) / SPLIT_ALIGN;
+    const int64_t cap = split_tree ? VA_MAX_SPLITS - 1 : VA_MAX_SPLITS;
     if (ns > max_ns) ns = max_ns;
-    if (ns > VA_MAX_SPLITS) ns = VA_MAX_SPLITS;
+    if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;
+    if (split_tree) ns += 1;   // the tree block
     p.num_tree[r] = h_num_tree[r];
     p.max_prefix[r] = h_prefix_len[r];
     p.nsplit[r] = (int32_t)ns;
@@ -955,8 +1044,15 @@ int verify_attn_run(const va_plan* plan, const uint16_t* q, const uint16_t* kv_p
     a.work_begin[r] = plan->work_begin[r];
   }
   const unsigned grid = 8u * (unsigned)((plan->total_work + 7) / 8);   // see the XCD work order
-  hipLaunchKernelGGL(va_partial_kernel, dim3(grid), dim3(THREADS), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan->mode == VA_MODE_SPLIT_TREE) {
+    int tree_blocks = 0;
+    for (int r = 0; r < plan->num_requests; ++r) tree_blocks += plan->num_groups[r];
+    hipLaunchKernelGGL(va_split_kernel, dim3(grid + (unsigned)tree_blocks), dim3(THREADS), 0, st,
+                       a, tree_blocks);
+  } else {
+    hipLaunchKernelGGL(va_partial_kernel, dim3(grid), dim3(THREADS), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 

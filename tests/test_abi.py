@@ -157,3 +157,55 @@ def test_run_argument_errors_are_caught_before_launch():
                                        ([-1, 1], False), ([-1, -2], False), ([-1] * 65, False)])
 def test_check_tree(parent, ok):
     assert (va.verify_attn_check_tree(parent) == 0) == ok
+
+
+# --------------------------------------------------------------------------- split-verify plans
+def test_plan_ex_without_flags_is_the_fused_plan():
+    a = _plan(8, [65536], [16])
+    lib = va.load_library()
+    b = binding.VaPlan()
+    pl = np.array([65536], np.int32)
+    nt = np.array([16], np.int32)
+    assert lib.verify_attn_plan_ex(1, 8, pl.ctypes.data_as(ctypes.c_void_p),
+                                   nt.ctypes.data_as(ctypes.c_void_p), 256, 0,
+                                   ctypes.byref(b), None) == 0
+    assert bytes(a) == bytes(b)
+    assert a.mode == binding.VA_MODE_FUSED and a.version == binding.VA_PLAN_VERSION
+
+
+def test_plan_split_tree_adds_one_tree_split_per_request():
+    p = va.verify_attn_plan(8, [65536], [16], num_cus=256, split_tree=True)
+    assert p.mode == binding.VA_MODE_SPLIT_TREE
+    # prefix keys x groups over the 254 CUs the 2 tree-block items leave:
+    # ceil(2 * 65536 / 254) = 517 keys per prefix split -> 127 prefix splits
+    assert p.nsplit[0] == 127 + 1
+    assert p.total_work == 2 * 128
+    o = 2 * 128 * 64 * 512 * 2
+    assert p.workspace_bytes == o + 2 * 128 * 64 * 8 + 1024
+    q = va.verify_attn_plan(4, [0, 100, 5000], [3, 64, 9], num_cus=256, split_tree=True)
+    assert all(ns >= 2 for ns in q.splits())                 # L = 0 keeps one (empty) prefix split
+    assert q.work_begin[3] == sum(q.num_groups[r] * q.nsplit[r] for r in range(3))
+
+
+def test_plan_split_tree_env_override_counts_prefix_splits(monkeypatch):
+    monkeypatch.setenv("VA_NSPLIT", "7")
+    p = va.verify_attn_plan(8, [65536], [16], num_cus=256, split_tree=True)
+    assert p.nsplit[0] == 8
+
+
+def test_plan_ex_rejects_unknown_flags_and_bad_modes():
+    lib = va.load_library()
+    b = binding.VaPlan()
+    pl = np.array([100], np.int32)
+    nt = np.array([4], np.int32)
+    assert lib.verify_attn_plan_ex(1, 8, pl.ctypes.data_as(ctypes.c_void_p),
+                                   nt.ctypes.data_as(ctypes.c_void_p), 256, 6,
+                                   ctypes.byref(b), None) == -2
+    plan = _plan(8, [100], [4])
+    bad = binding.VaPlan()
+    ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
+    bad.mode = 7
+    assert _run(lib, bad) == -5
+    bad.mode = binding.VA_MODE_SPLIT_TREE           # a split-tree plan needs >= 2 splits
+    bad.nsplit[0] = 1
+    assert _run(lib, bad) == -5
