@@ -66,6 +66,100 @@ def traffic_from_profile():
     return float(val.group(1))
 
 
+def capture_timer(torch, stream):
+    """Returns time_graph(fn, n): ms per call of fn(i), i < n, captured in one
+    HIP graph and replayed between two events on `stream`."""
+    def time_graph(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    return time_graph
+
+
+def measure_defrag(torch, va, wl, pools, table, indptr, prefix, parent, q, H, K, stream,
+                   time_graph):
+    """Tier 1 defrag on the bench request: the compaction kernel's time, and
+    verify on the fragmented table against the compacted one.  Each pool copy
+    gets a free run of n slots appended; the compacted rows land there."""
+    n = int(table.numel())
+    base = pools[0].shape[0]
+    ext = [torch.cat([p, torch.zeros((n, p.shape[1]), dtype=p.dtype, device=p.device)])
+           for p in pools]
+    frag = table.clone()
+    work = table.clone()
+    lib = va.load_library()
+    ws = torch.empty(int(lib.verify_attn_compact_workspace_bytes(n, n)), dtype=torch.uint8,
+                     device=table.device)
+    copied = torch.empty(1, dtype=torch.int32, device=table.device)
+
+    def restore(i):
+        work.copy_(frag)
+
+    def restore_and_compact(i):
+        work.copy_(frag)
+        va.verify_attn_compact(ext[i % len(ext)], work, base, n, workspace=ws, copied=copied,
+                               stream=stream)
+
+    reps = max(8, min(K, 64))
+    ms_restore = time_graph(restore, reps)
+    ms_compact = time_graph(restore_and_compact, reps) - ms_restore
+    assert int(copied.item()) == n
+    compacted = work.clone()                      # base .. base + n - 1
+    with torch.cuda.stream(stream):               # every pool copy holds the compacted rows
+        for p in ext:
+            work.copy_(frag)
+            va.verify_attn_compact(p, work, base, n, workspace=ws, copied=copied, stream=stream)
+    torch.cuda.synchronize()
+    plan = va.verify_attn_plan(H, wl.prefix_len, wl.num_tree)
+    vws = va.workspace_for(plan, table.device)
+    out = torch.empty((int(plan.total_tree), H, 512), dtype=torch.bfloat16, device=table.device)
+    lse = torch.empty((int(plan.total_tree), H), dtype=torch.float32, device=table.device)
+
+    def verify_with(tab):
+        def fn(i):
+            va.verify_attn_run(plan, q, ext[i % len(ext)], tab, indptr, prefix, parent,
+                               wl.sm_scale, vws, stream)
+            va.verify_attn_reduce(plan, vws, out, lse, stream)
+        return fn
+
+    ms_frag = time_graph(verify_with(frag), K)
+    o_frag = out.clone()
+    ms_comp = time_graph(verify_with(compacted), K)
+    same = bool(torch.equal(o_frag.view(torch.int16), out.view(torch.int16)))
+    kv_bytes = wl.kv_bytes()
+
+    def runs(t):   # maximal runs of consecutive slots
+        t = t.cpu().numpy().astype(np.int64)
+        return 1 + int(np.count_nonzero(t[1:] != t[:-1] + 1)) if len(t) else 0
+
+    return {
+        "policy": "rows moved to a reserved free run in logical order, budget = all rows",
+        "rows": n,
+        "runs_before": runs(frag),
+        "runs_after": runs(compacted),
+        "compact_us": round(ms_compact * 1e3, 3),
+        "compact_copy_gbs": round(2 * n * 1152 / (ms_compact * 1e-3) / 1e9, 1),
+        "verify_fragmented_us": round(ms_frag * 1e3, 3),
+        "verify_compacted_us": round(ms_comp * 1e3, 3),
+        "verify_fragmented_gbs": round(kv_bytes / (ms_frag * 1e-3) / 1e9, 2),
+        "verify_compacted_gbs": round(kv_bytes / (ms_comp * 1e-3) / 1e9, 2),
+        "outputs_bitwise_equal": same,
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,6 +174,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch without graph capture")
     ap.add_argument("--no-stream-peak", action="store_true",
                     help="skip the 2 GiB streaming-read calibration")
+    ap.add_argument("--no-defrag", action="store_true",
+                    help="skip the compaction (Tier 1 defrag) measurement")
     return ap.parse_args()
 
 
@@ -199,6 +295,11 @@ def main():
         torch.cuda.synchronize()
         print(f"# calibration copy of {nbytes} bytes x3 done", file=sys.stderr, flush=True)
 
+    defrag = None
+    if not args.no_defrag:
+        defrag = measure_defrag(torch, va, wl, pools[:4], table, indptr, prefix, parent, q, H,
+                                K, stream, capture_timer(torch, stream))
+
     stream_peak = None
     if not args.no_stream_peak:
         # measured read ceiling of this GPU: a plain torch reduction over 2 GiB
@@ -287,6 +388,7 @@ def main():
             "nsplit": plan_split.splits(),
             "max_abs_out_vs_fused": split_vs_fused,
         },
+        "defrag": defrag,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "wall_s_timed": round(t_wall, 3),

@@ -246,6 +246,47 @@ const char* verify_attn_error_string(int code);
  * their mirror of the struct. */
 size_t verify_attn_plan_struct_size(void);
 
+/*
+ * ---- Tier 1 KV defragmentation: compaction of one request's slots ----
+ *
+ * "The Execution Phase" (section "Tier 0 KV Defragmentation") names live
+ * relocation of a request's fragmented KV slots under a copy budget as the
+ * next tier; "The Architecture Detective" (section "Deconstructing the K/V
+ * Defrag Hypothesis") describes moving a request's KV entries to contiguous
+ * slots.  Policy (the plainest reading): logical position k of the table
+ * belongs at slot dst_begin + k of a free run [dst_begin, dst_begin + n)
+ * the caller reserved.  Walking k upward, each row not yet at its place is
+ * copied there (its 576 columns) and table[k] rewritten,
+ * until `budget` rows have been copied; rows already in place are skipped
+ * and do not count.
+ *
+ * kv_pool        [num_slots, kv_row_stride] bf16, device, 16-byte aligned;
+ *                the copied rows' first 576 columns are written.
+ * slot_table     [n] int32, device: one request's table (prefix then draft
+ *                entries, or any other run of logical positions); rewritten.
+ *                May be NULL when n = 0 (then copied is set to 0).
+ * dst_begin      first slot of the reserved run; dst_begin + n <= num_slots.
+ * budget         most rows to copy (>= 0).
+ * workspace      device, 256-byte aligned, at least
+ *                verify_attn_compact_workspace_bytes(n, budget) bytes.
+ * copied         device int32 out: rows copied, or minus the OR of the
+ *                VA_COMPACT_* bits when a precondition failed (then nothing
+ *                is copied and the table is unchanged).
+ * Preconditions checked on the device: every slot inside the pool, and no
+ * slot inside the destination run except at its own place (such a row could
+ * be overwritten before it is read).  Stream-ordered, asynchronous,
+ * graph-capture safe (grids depend on n and budget only).
+ * Errors (host): VA_ERR_NULL, VA_ERR_SHAPE (negative sizes, run outside the
+ * pool, stride < 576), VA_ERR_ALIGN, VA_ERR_WORKSPACE, VA_ERR_HIP.
+ */
+#define VA_COMPACT_BAD_SLOT 1u       /* a slot outside [0, num_slots) */
+#define VA_COMPACT_RUN_OCCUPIED 2u   /* a slot inside the run but not at its own place */
+size_t verify_attn_compact_workspace_bytes(int32_t n, int32_t budget);
+int verify_attn_compact(uint16_t* kv_pool, int64_t num_slots, int32_t kv_row_stride,
+                        int32_t* slot_table, int32_t n, int32_t dst_begin, int32_t budget,
+                        void* workspace, size_t workspace_bytes, int32_t* copied,
+                        va_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

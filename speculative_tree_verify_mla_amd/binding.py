@@ -40,8 +40,9 @@ EXPORTS = (
     "verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
     "verify_attn_read_status",
     "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_error_string",
-    "verify_attn_plan_struct_size",
+    "verify_attn_plan_struct_size", "verify_attn_compact_workspace_bytes", "verify_attn_compact",
 )
+COMPACT_BITS = {1: "BAD_SLOT", 2: "RUN_OCCUPIED"}
 
 
 class VaPlan(ctypes.Structure):
@@ -100,6 +101,10 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_gather_rows.argtypes = [P, i64, i32, P, i32, P, P]
     lib.verify_attn_error_string.argtypes = [ctypes.c_int]
     lib.verify_attn_error_string.restype = ctypes.c_char_p
+    lib.verify_attn_compact_workspace_bytes.argtypes = [i32, i32]
+    lib.verify_attn_compact_workspace_bytes.restype = sz
+    lib.verify_attn_compact.argtypes = [P, i64, i32, P, i32, i32, i32, P, sz, P, P]
+    lib.verify_attn_compact.restype = ctypes.c_int
     lib.verify_attn_plan_struct_size.argtypes = []
     lib.verify_attn_plan_struct_size.restype = sz
     for name in ("verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
@@ -240,6 +245,36 @@ def verify_attn_gather_rows(kv_pool, slot_table, n, dst, stream=None):
 
 def verify_attn_error_string(code) -> str:
     return load_library().verify_attn_error_string(int(code)).decode()
+
+
+def verify_attn_compact(kv_pool, slot_table, dst_begin, budget, workspace=None, copied=None,
+                        stream=None):
+    """Enqueue the compaction of one request's slot table (rewritten in place)
+    into the run [dst_begin, dst_begin + n) of kv_pool, copying at most
+    `budget` rows.  Returns the device int32 tensor [1] of rows copied (or
+    minus the VA_COMPACT_* bits of a failed precondition)."""
+    import torch
+    if kv_pool.dim() != 2 or kv_pool.shape[1] < VA_D_QK or kv_pool.stride(1) != 1:
+        raise ValueError("kv_pool must be [num_slots, >=576] with unit column stride")
+    if not kv_pool.is_cuda or kv_pool.dtype not in _bf16_types():
+        raise TypeError("kv_pool must be a bf16 (or 16-bit integer) device tensor")
+    if slot_table.dim() != 1:
+        raise ValueError("slot_table must be one request's [n] table")
+    n = int(slot_table.numel())
+    lib = load_library()
+    if workspace is None:
+        workspace = torch.empty(int(lib.verify_attn_compact_workspace_bytes(n, int(budget))),
+                                dtype=torch.uint8, device=kv_pool.device)
+    if copied is None:
+        copied = torch.empty(1, dtype=torch.int32, device=kv_pool.device)
+    rc = lib.verify_attn_compact(
+        ctypes.c_void_p(kv_pool.data_ptr()),
+        int(kv_pool.shape[0]), int(kv_pool.stride(0)),
+        _dptr(slot_table, (torch.int32,), "slot_table"), n, int(dst_begin), int(budget),
+        _dptr(workspace, (torch.uint8,), "workspace"), int(workspace.numel()),
+        _dptr(copied, (torch.int32,), "copied"), _stream_handle(stream))
+    _check("verify_attn_compact", rc)
+    return copied
 
 
 # --------------------------------------------------------------------------- convenience
