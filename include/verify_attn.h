@@ -287,6 +287,43 @@ int verify_attn_compact(uint16_t* kv_pool, int64_t num_slots, int32_t kv_row_str
                         void* workspace, size_t workspace_bytes, int32_t* copied,
                         va_stream_t stream);
 
+/*
+ * ---- Draft-tree marshaling on the device ----
+ *
+ * The pages build the draft tree and its mask on the host ("The Execution
+ * Phase", section "The Methodology: Evidence-Driven Engineering": 1.8 ms of
+ * tree build and 0.18 ms of mask build per step); this call does it on the
+ * device so a whole verify step can live in one HIP graph.
+ *
+ * For request r of `plan` (its T_r = num_tree[r] and tree_begin layout):
+ * raw_parent     [sum T_r] device: request-local parent of raw node j, in
+ *                [-1, T_r) (-1: hangs off the prefix), nodes in any order.
+ * raw_slot       [sum T_r] device: pool slot holding raw node j's KV row.
+ * prefix_len, slot_indptr   as for verify_attn_run (device).
+ * slot_table     device, slot_table_len entries: receives, for verify
+ *                position i, slot_table[slot_indptr[r] + prefix_len[r] + i]
+ *                = raw_slot[perm[i]] (only inside [slot_indptr[r],
+ *                slot_indptr[r+1])).
+ * perm, parent   [sum T_r] int32 out: verify order = raw nodes sorted by
+ *                (depth, raw index), i.e. breadth first, so parent[i] < i;
+ *                perm[i] is the raw node at position i, parent[i] its
+ *                parent's position or -1 - ready for verify_attn_run.
+ * anc            [sum T_r] uint64 out: bit k set iff position k is i or an
+ *                ancestor of i (the tree mask, as the kernel uses it).
+ * status         [B] uint32 out: 0, or VA_TREE_* bits for a request whose
+ *                raw tree is not a forest or whose table range is too short
+ *                (then its outputs are unspecified; other requests are not
+ *                affected).
+ * One 64-lane wave per request; stream-ordered, graph-capture safe.
+ * Errors (host): VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_SHAPE, VA_ERR_HIP.
+ */
+#define VA_TREE_BAD_PARENT 1u   /* a parent outside [-1, T_r) or a cycle */
+#define VA_TREE_BAD_TABLE 2u    /* a draft entry falls outside the request's table range */
+int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const int32_t* raw_slot,
+                           const int32_t* prefix_len, const int32_t* slot_indptr,
+                           int32_t* slot_table, int32_t slot_table_len, int32_t* perm,
+                           int32_t* parent, uint64_t* anc, uint32_t* status, va_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

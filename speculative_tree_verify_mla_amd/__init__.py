@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     VerifyAttnError,
     load_library,
     verify_attn,
+    verify_attn_build_tree,
     verify_attn_check_tree,
     verify_attn_compact,
     verify_attn_error_string,

@@ -7,7 +7,7 @@ from pathlib import Path
 
 PKG_DIR = Path(__file__).resolve().parent
 REPO_DIR = PKG_DIR.parent
-SOURCES = [PKG_DIR / "csrc" / "verify_attn.hip", PKG_DIR / "csrc" / "compact.hip"]
+SOURCES = [PKG_DIR / "csrc" / n for n in ("verify_attn.hip", "compact.hip", "tree.hip")]
 INCLUDE_DIR = REPO_DIR / "include"
 LIB_PATH = PKG_DIR / "libverify_attn.so"
 ARCH = "gfx950"

@@ -41,7 +41,9 @@ EXPORTS = (
     "verify_attn_read_status",
     "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_error_string",
     "verify_attn_plan_struct_size", "verify_attn_compact_workspace_bytes", "verify_attn_compact",
+    "verify_attn_build_tree",
 )
+TREE_BITS = {1: "BAD_PARENT", 2: "BAD_TABLE"}
 COMPACT_BITS = {1: "BAD_SLOT", 2: "RUN_OCCUPIED"}
 
 
@@ -105,6 +107,8 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_compact_workspace_bytes.restype = sz
     lib.verify_attn_compact.argtypes = [P, i64, i32, P, i32, i32, i32, P, sz, P, P]
     lib.verify_attn_compact.restype = ctypes.c_int
+    lib.verify_attn_build_tree.argtypes = [ctypes.POINTER(VaPlan), P, P, P, P, P, i32, P, P, P, P, P]
+    lib.verify_attn_build_tree.restype = ctypes.c_int
     lib.verify_attn_plan_struct_size.argtypes = []
     lib.verify_attn_plan_struct_size.restype = sz
     for name in ("verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
@@ -275,6 +279,32 @@ def verify_attn_compact(kv_pool, slot_table, dst_begin, budget, workspace=None, 
         _dptr(copied, (torch.int32,), "copied"), _stream_handle(stream))
     _check("verify_attn_compact", rc)
     return copied
+
+
+def verify_attn_build_tree(plan, raw_parent, raw_slot, prefix_len, slot_indptr, slot_table,
+                           stream=None):
+    """Enqueue the device marshaling of raw draft trees (any node order) into
+    verify order.  Writes the draft entries of slot_table in place; returns
+    device tensors (perm int32, parent int32, anc int64 bit masks, status
+    uint32 per request -- stored as int32)."""
+    import torch
+    dev = raw_parent.device
+    n = int(plan.total_tree)
+    if raw_parent.numel() != n or raw_slot.numel() != n:
+        raise ValueError("raw_parent and raw_slot need sum(T_r) entries")
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    parent = torch.empty(n, dtype=torch.int32, device=dev)
+    anc = torch.empty(n, dtype=torch.int64, device=dev)
+    status = torch.empty(int(plan.num_requests), dtype=torch.int32, device=dev)
+    i32 = (torch.int32,)
+    rc = load_library().verify_attn_build_tree(
+        ctypes.byref(plan), _dptr(raw_parent, i32, "raw_parent"), _dptr(raw_slot, i32, "raw_slot"),
+        _dptr(prefix_len, i32, "prefix_len"), _dptr(slot_indptr, i32, "slot_indptr"),
+        _dptr(slot_table, i32, "slot_table"), int(slot_table.numel()),
+        _dptr(perm, i32, "perm"), _dptr(parent, i32, "parent"),
+        _dptr(anc, (torch.int64,), "anc"), _dptr(status, i32, "status"), _stream_handle(stream))
+    _check("verify_attn_build_tree", rc)
+    return perm, parent, anc, status
 
 
 # --------------------------------------------------------------------------- convenience

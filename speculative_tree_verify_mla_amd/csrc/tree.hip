@@ -1,0 +1,152 @@
+// tree.hip - draft-tree marshaling on the GPU.
+//
+// The verify call needs, per request, the draft nodes in an order where every
+// parent precedes its children, the parent array in that order, and the
+// slot-table entries of the draft tokens after the prefix.  The pages build
+// the tree and its mask on the host ("The Execution Phase", section "The
+// Methodology: Evidence-Driven Engineering": tree build 1.8 ms and mask build
+// 0.18 ms of CPU time per step); doing it on the device keeps the whole
+// verify step inside one HIP graph.
+//
+// Input per request r (T_r <= 64 nodes): raw_parent[j] in [-1, T_r) for raw
+// node j in any order (-1: attached to the prefix), and raw_slot[j], the pool
+// slot holding node j's KV row.  Output, in verify order = sorted by (depth,
+// raw index) (breadth first, so parents come first):
+//   perm[i]       raw node at verify position i
+//   parent[i]     verify position of its parent, or -1
+//   anc[i]        bit k set iff verify node k is i or an ancestor of i
+//   slot_table[slot_indptr[r] + prefix_len[r] + i] = raw_slot[perm[i]]
+// One wave per request, lane j = raw node j.  A parent outside [-1, T_r) or
+// a cycle sets the request's status bit (VA_TREE_BAD_PARENT); its outputs are
+// then unspecified, and nothing is written outside the request's own ranges.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "verify_attn.h"
+
+namespace {
+
+struct TreeArgs {
+  const int32_t* raw_parent;   // [sum T_r]
+  const int32_t* raw_slot;     // [sum T_r]
+  const int32_t* prefix_len;   // [B]
+  const int32_t* slot_indptr;  // [B+1]
+  int32_t* slot_table;
+  int32_t slot_table_len;
+  int32_t num_requests;
+  int32_t* perm;               // [sum T_r]
+  int32_t* parent;             // [sum T_r]
+  uint64_t* anc;               // [sum T_r]
+  uint32_t* status;            // [B]
+  int32_t tree_begin[VA_MAX_REQUESTS + 1];
+};
+
+__global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
+  const int r = blockIdx.x;
+  if (r >= a.num_requests) return;
+  const int lane = threadIdx.x;
+  const int t0 = a.tree_begin[r];
+  const int T = a.tree_begin[r + 1] - t0;
+  const bool live = lane < T;
+  uint32_t bad = 0u;
+
+  // depth by walking up the chain; a walk longer than T means a cycle
+  int p = live ? a.raw_parent[t0 + lane] : -1;
+  if (live && (p < -1 || p >= T)) {
+    bad = VA_TREE_BAD_PARENT;
+    p = -1;
+  }
+  int depth = 0;
+  {
+    int x = p;
+    while (live && x != -1 && bad == 0u) {
+      ++depth;
+      if (depth > T) {
+        bad = VA_TREE_BAD_PARENT;
+        break;
+      }
+      const int px = a.raw_parent[t0 + x];
+      if (px < -1 || px >= T) {
+        bad = VA_TREE_BAD_PARENT;
+        break;
+      }
+      x = px;
+    }
+  }
+  // verify position = rank of (depth, raw index) among the live nodes
+  const int key = live ? (depth << 6) | lane : 0x7fffffff;
+  int rank = 0;
+  for (int k = 0; k < 64; ++k) rank += __shfl(key, k) < key ? 1 : 0;
+  const int prank = __shfl(rank, p < 0 ? 0 : p);
+  // ancestor mask in verify positions: walk the chain again, mapping raw ids
+  // to verify positions through the wave (every lane takes part in the
+  // shuffles; lanes with x = -1 idle)
+  uint64_t m = 0ull;
+  {
+    int x = (live && bad == 0u) ? lane : -1;
+    for (int step = 0; step < 64; ++step) {
+      const int rx = __shfl(rank, x < 0 ? 0 : x);
+      const int nx = __shfl(p, x < 0 ? 0 : x);
+      if (x >= 0) {
+        m |= 1ull << (rx & 63);
+        x = nx;
+      }
+    }
+  }
+  if (live) {
+    const int o = t0 + rank;
+    a.perm[o] = lane;
+    a.parent[o] = p < 0 ? -1 : prank;
+    a.anc[o] = m;
+    const int64_t e = (int64_t)a.slot_indptr[r] + a.prefix_len[r] + rank;
+    if (e >= 0 && e < a.slot_table_len && e < a.slot_indptr[r + 1])
+      a.slot_table[e] = a.raw_slot[t0 + lane];
+    else
+      bad |= VA_TREE_BAD_TABLE;
+  }
+  uint32_t bits = bad;
+  for (int o = 32; o >= 1; o >>= 1) bits |= __shfl_xor(bits, o);
+  if (lane == 0) a.status[r] = bits;
+}
+
+}  // namespace
+
+extern "C" {
+
+int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const int32_t* raw_slot,
+                           const int32_t* prefix_len, const int32_t* slot_indptr,
+                           int32_t* slot_table, int32_t slot_table_len, int32_t* perm,
+                           int32_t* parent, uint64_t* anc, uint32_t* status, va_stream_t stream) {
+  if (plan == nullptr || raw_parent == nullptr || raw_slot == nullptr || prefix_len == nullptr ||
+      slot_indptr == nullptr || slot_table == nullptr || perm == nullptr || parent == nullptr ||
+      anc == nullptr || status == nullptr)
+    return VA_ERR_NULL;
+  if (plan->magic != VA_PLAN_MAGIC || plan->version != VA_PLAN_VERSION ||
+      plan->num_requests < 1 || plan->num_requests > VA_MAX_REQUESTS)
+    return VA_ERR_PLAN;
+  for (int r = 0; r < plan->num_requests; ++r)
+    if (plan->num_tree[r] < 1 || plan->num_tree[r] > VA_MAX_TREE ||
+        plan->tree_begin[r + 1] - plan->tree_begin[r] != plan->num_tree[r])
+      return VA_ERR_PLAN;
+  if (slot_table_len < 0) return VA_ERR_SHAPE;
+  TreeArgs a;
+  a.raw_parent = raw_parent;
+  a.raw_slot = raw_slot;
+  a.prefix_len = prefix_len;
+  a.slot_indptr = slot_indptr;
+  a.slot_table = slot_table;
+  a.slot_table_len = slot_table_len;
+  a.num_requests = plan->num_requests;
+  a.perm = perm;
+  a.parent = parent;
+  a.anc = anc;
+  a.status = status;
+  for (int r = 0; r <= plan->num_requests; ++r) a.tree_begin[r] = plan->tree_begin[r];
+  hipLaunchKernelGGL(build_tree_kernel, dim3(plan->num_requests), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+"""GPU draft-tree marshaling (verify_attn_build_tree) against the plain
+reference oracle.tree, bit for bit, and end to end through the verify call."""
+import numpy as np
+import pytest
+import torch
+
+import speculative_tree_verify_mla_amd as va
+from oracle import tree as ot
+from speculative_tree_verify_mla_amd import inputs
+from test_parity import DEV, Dev, _t, check, say
+from test_tree_oracle import _golden
+
+pytestmark = pytest.mark.gpu
+
+
+def _raw_batch(num_tree, prefix, seed, slots=4096):
+    """A workload whose trees are relabeled at random: returns (workload,
+    raw_parent, raw_slot, q in raw order) with the draft table entries
+    blanked out."""
+    rng = np.random.default_rng(seed)
+    wl = inputs.make_workload("mar", 4, num_tree, prefix, slots, seed=seed,
+                              table="interleaved" if len(num_tree) > 1 else "scattered")
+    raw_parent = np.empty_like(wl.parent)
+    raw_slot = np.empty_like(wl.parent)
+    q_raw = np.empty_like(wl.q)
+    t0 = 0
+    for r, T in enumerate(wl.num_tree):
+        sigma = rng.permutation(T)
+        base = int(wl.slot_indptr[r]) + int(wl.prefix_len[r])
+        for g in range(T):
+            pg = wl.parent[t0 + g]
+            raw_parent[t0 + sigma[g]] = -1 if pg == -1 else sigma[pg]
+            raw_slot[t0 + sigma[g]] = wl.slot_table[base + g]
+            q_raw[t0 + sigma[g]] = wl.q[t0 + g]
+        t0 += T
+    return wl, raw_parent, raw_slot, q_raw
+
+
+def _gpu_marshal(wl, raw_parent, raw_slot, table):
+    plan = va.verify_attn_plan(wl.num_heads, wl.prefix_len, wl.num_tree)
+    tab = _t(table)
+    perm, parent, anc, status = va.verify_attn_build_tree(
+        plan, _t(raw_parent), _t(raw_slot), _t(wl.prefix_len), _t(wl.slot_indptr), tab)
+    torch.cuda.synchronize()
+    return (perm.cpu().numpy(), parent.cpu().numpy(), anc.cpu().numpy().view(np.uint64),
+            status.cpu().numpy().view(np.uint32), tab.cpu().numpy(), plan)
+
+
+@pytest.mark.parametrize("num_tree,prefix", [([1], [10]), ([5], [0]), ([16], [300]),
+                                             ([64], [1000]), ([3, 33, 1, 64], [5, 70, 0, 400])])
+def test_marshaling_matches_the_reference(num_tree, prefix):
+    wl, rp, rs, _ = _raw_batch(num_tree, prefix, seed=sum(num_tree))
+    table = wl.slot_table.copy()
+    for r in range(len(num_tree)):
+        b = int(wl.slot_indptr[r]) + int(wl.prefix_len[r])
+        table[b:b + num_tree[r]] = -7
+    ref = ot.marshal(wl.num_tree, rp, rs, wl.prefix_len, wl.slot_indptr, table)
+    got = _gpu_marshal(wl, rp, rs, table)
+    say(f"  marshal T={num_tree} status={got[3].tolist()}")
+    for name, a, b in zip(("perm", "parent", "anc", "status", "table"), got[:5], ref):
+        np.testing.assert_array_equal(a, b, err_msg=name)
+    # the same draft slots come back, in breadth-first order of the tree
+    np.testing.assert_array_equal(np.sort(got[4]), np.sort(wl.slot_table))
+
+
+def test_hand_worked_trees_on_the_gpu():
+    cases = _golden()
+    num_tree = [len(c["raw_parent"]) for c in cases]
+    wl = inputs.make_workload("g", 1, num_tree, [2] * len(cases), 256, seed=3, table="interleaved")
+    rp = np.concatenate([np.array(c["raw_parent"], np.int32) for c in cases])
+    rs = np.arange(len(rp), dtype=np.int32) + 100
+    perm, parent, anc, status, _, _ = _gpu_marshal(wl, rp, rs, wl.slot_table.copy())
+    assert (status == 0).all()
+    t0 = 0
+    for c, T in zip(cases, num_tree):
+        assert perm[t0:t0 + T].tolist() == c["perm"], c["name"]
+        assert parent[t0:t0 + T].tolist() == c["parent"], c["name"]
+        for i, pos in c["anc"].items():
+            assert int(anc[t0 + i]) == sum(1 << k for k in pos), (c["name"], i)
+        t0 += T
+
+
+def test_bad_trees_are_flagged_per_request():
+    wl, rp, rs, _ = _raw_batch([6, 6, 6], [20, 30, 40], seed=11)
+    rp = rp.copy()
+    rp[0:2] = [1, 0]                      # request 0: a cycle
+    rp[6 + 3] = 6                         # request 1: parent out of range
+    ref = ot.marshal(wl.num_tree, rp, rs, wl.prefix_len, wl.slot_indptr, wl.slot_table)
+    got = _gpu_marshal(wl, rp, rs, wl.slot_table.copy())
+    assert got[3][0] & ot.BAD_PARENT and got[3][1] & ot.BAD_PARENT and got[3][2] == 0
+    for k in range(3):                    # request 2 is exact
+        np.testing.assert_array_equal(got[k][12:], ref[k][12:])
+    short = wl.slot_indptr.copy()
+    short[3] -= 2                         # request 2's table range is 2 entries short
+    wl2 = inputs.Workload(**{**wl.__dict__, "slot_indptr": short})
+    got2 = _gpu_marshal(wl2, rp, rs, wl.slot_table.copy())
+    assert got2[3][2] & ot.BAD_TABLE
+
+
+def test_marshal_then_verify_in_one_graph():
+    """Raw trees in, verify outputs out, all captured in one HIP graph; rows
+    come out in verify order and match the oracle on the marshaled inputs."""
+    wl, rp, rs, q_raw = _raw_batch([16, 9], [700, 1200], seed=21)
+    d = Dev(wl)
+    table = wl.slot_table.copy()
+    for r in range(2):
+        b = int(wl.slot_indptr[r]) + int(wl.prefix_len[r])
+        table[b:b + int(wl.num_tree[r])] = -7
+    d.table = _t(table)
+    plan = va.verify_attn_plan(wl.num_heads, wl.prefix_len, wl.num_tree)
+    ws = va.workspace_for(plan, DEV)
+    raw_p, raw_s = _t(rp), _t(rs)
+    qr = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    qv = torch.empty_like(qr)
+    H = wl.num_heads
+    out = torch.empty((25, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((25, H), dtype=torch.float32, device=DEV)
+    base = torch.tensor([0] * 16 + [16] * 9, dtype=torch.int64, device=DEV)   # request offsets
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            perm, parent, anc, status = va.verify_attn_build_tree(
+                plan, raw_p, raw_s, d.prefix, d.indptr, d.table, stream=st)
+            qv.copy_(qr.index_select(0, perm.long() + base))
+            va.verify_attn(qv, d.kv, d.table, d.indptr, d.prefix, parent, wl.sm_scale,
+                           num_tree=wl.num_tree, prefix_len_host=wl.prefix_len, plan=plan,
+                           workspace=ws, out=out, lse=lse, stream=st)
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    ref = ot.marshal(wl.num_tree, rp, rs, wl.prefix_len, wl.slot_indptr, table)
+    np.testing.assert_array_equal(d.table.cpu().numpy(), ref[4])
+    perm_h = ref[0]
+    q_v = np.concatenate([q_raw[:16][perm_h[:16]], q_raw[16:][perm_h[16:]]])
+    wl_v = inputs.Workload(**{**wl.__dict__, "q": q_v, "parent": ref[1], "slot_table": ref[4]})
+    check(wl_v, out, lse, what="marshal+verify graph", raw=True)
