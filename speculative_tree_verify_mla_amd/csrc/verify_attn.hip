@@ -349,23 +349,42 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   const int ntiles = k1 > k0 ? (k1 - k0 + TILE - 1) / TILE : 0;
   const int32_t* table = a.slot_table + (n_valid > 0 ? tab0 : 0);
 
-  // ---- ancestor masks (bit j of anc[i]: draft node j is i or an ancestor of i)
-  if (MODE != PREFIX && tid < VA_MAX_TREE) {
-    uint64_t m = 0;
-    if (tid < T) {
-      const int32_t* par = a.parent + a.tree_begin[r];
-      int x = tid;
-      while (x != -1) {
+  // ---- slot-table entries of the first two tiles: the first copies wait on
+  // them, so they go out before everything else.  Wave 0 copies the 64
+  // entries of tile u into sring[u % SLOT_RING] (one 4-byte copy per lane;
+  // keys past the split end read the split's last entry, which is in bounds).
+  auto issue_slots = [&](int u) {
+    if (wave == 0) {
+      const int k = min(k0 + u * TILE + lane, k1 - 1);
+      dma4_v(lds_addr(&sring[u & (SLOT_RING - 1)][0]), table + k);
+    }
+  };
+  if (ntiles > 0) {
+    issue_slots(0);
+    issue_slots(1);
+  }
+
+  // ---- ancestor masks (bit j of anc[i]: draft node j is i or an ancestor of
+  // i).  Lane i of wave 0 holds node i's parent; the chains are followed
+  // through the wave, so the parent array is read once.
+  if (MODE != PREFIX && wave == 0) {
+    const int32_t* par = a.parent + a.tree_begin[r];
+    int p = lane < T ? par[lane] : -1;
+    if (p < -1 || p >= lane) {   // parents precede their children
+      st |= VA_STATUS_BAD_PARENT;
+      p = -1;
+    }
+    uint64_t m = lane < T ? 1ull << lane : 0ull;
+    // every step moves to a smaller index, so the walk ends within T steps
+    int x = p;
+    while (__any(x >= 0)) {
+      const int nx = __shfl(p, x >= 0 ? x : 0);
+      if (x >= 0) {
         m |= 1ull << x;
-        const int p = par[x];
-        if (p < -1 || p >= x) {   // also guarantees the walk ends
-          st |= VA_STATUS_BAD_PARENT;
-          break;
-        }
-        x = p;
+        x = nx;
       }
     }
-    anc[tid] = m;
+    anc[lane] = m;
   }
 
   // ---- Q fragments of this lane's row over all 576 score columns
@@ -383,20 +402,11 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     }
   }
 
-  // ---- tile loader.  Wave 0 copies the 64 slot-table entries of tile u into
-  // sring[u % SLOT_RING] (one 4-byte copy per lane; keys past the split end
-  // read the split's last entry, which is in bounds).  For tile u, lane l
-  // takes the slot of key l from the ring; wave w copies the latent rows of
-  // keys 16w .. 16w+15 (one 1 KB copy each) and the rope parts of the same
-  // keys (two copies of 8 rows).  Keys past the split end and slots outside
-  // the pool copy the zero row.
+  // ---- tile loader.  For tile u, lane l takes the slot of key l from the
+  // ring; wave w copies the latent rows of keys 16w .. 16w+15 (one 1 KB copy
+  // each) and the rope parts of the same keys (two copies of 8 rows).  Keys
+  // past the split end and slots outside the pool copy the zero row.
   uint32_t bad = 0u;
-  auto issue_slots = [&](int u) {
-    if (wave == 0) {
-      const int k = min(k0 + u * TILE + lane, k1 - 1);
-      dma4_v(lds_addr(&sring[u & (SLOT_RING - 1)][0]), table + k);
-    }
-  };
   // The copies of a tile are issued in ISSUE_PARTS pieces spread over the
   // score MFMAs of the previous tile: a burst of all of them stalls the wave
   // on memory back-pressure while the MFMA pipe idles.
@@ -405,9 +415,10 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     uint64_t use;    // bit j: key j is read (exists and its slot is in the pool)
     uint32_t lbuf;   // LDS byte address of the tile buffer
   };
-  auto prepare_tile = [&](int u, uint16_t* buf) -> TileIssue {
+  // vslot: sring[u % SLOT_RING][lane], read ahead by the caller
+  auto prepare_tile = [&](int u, int32_t vslot, uint16_t* buf) -> TileIssue {
     TileIssue ti;
-    ti.vslot = sring[u & (SLOT_RING - 1)][lane];
+    ti.vslot = vslot;
     const int k = k0 + u * TILE + lane;
     const bool exists = k < k1;
     const bool inside = ti.vslot >= 0 && (int64_t)ti.vslot < a.num_slots;
@@ -513,7 +524,11 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     float mx = sacc[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));   // this wave's 32 keys of the row
+    {   // this wave's 32 keys of the row: lanes l and l ^ 32 hold the two halves
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                       __builtin_bit_cast(uint32_t, mx), false, false);
+      mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+    }
     mx *= a.scale_log2;
     m_seen = fmaxf(m_seen, mx);
     if (first) {
@@ -605,7 +620,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     l_run = 0.f;
     lb_run = 0.f;
     if (tid == 0) restart_sh = 0u;
-    if (ntiles > 0) {
+    if (ntiles > 0 && pass > 0) {   // the first pass's went out at the start
       issue_slots(0);
       issue_slots(1);
     }
@@ -615,27 +630,35 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     __syncthreads();   // slots 0, 1, anc[], status_sh and restart_sh ready
     if (pass == 0 && MODE != PREFIX) anc_row = row_ok ? anc[rho / H] : 0ull;
     if (ntiles > 0) {
-      const TileIssue first_tile = prepare_tile(0, tiles);
+      const TileIssue first_tile = prepare_tile(0, sring[0][lane], tiles);
 #pragma unroll
       for (int g = 0; g < 9; ++g) issue_part(first_tile, g);
       issue_slots(2);
     }
 
     bool restart = false;
+    bool restart_seen = false;   // restart_sh as of the last mid-tile barrier
+    // slots of tile 1 (landed before the barrier above); each iteration reads
+    // the slots of the tile after next, which landed at its top wait
+    int32_t vslot_next = sring[1][lane];
     for (int t = 0; t < ntiles; ++t) {
       vm_wait<0>();
       lds_barrier();   // tile t is in LDS; every wave is done with tile t-1
-      if (restart_sh != 0u && pass + 1 < MAX_PASSES) {   // uniform: read after the barrier
+      if (restart_seen && pass + 1 < MAX_PASSES) {   // uniform
         restart = true;
         break;
       }
       // the next tile's copies; after the last tile they copy the zero row
       // (every key lies past the split end) into the free buffer
-      const TileIssue nxt = prepare_tile(t + 1, tiles + ((t + 1) & 1) * BUF_ELEMS);
+      const TileIssue nxt = prepare_tile(t + 1, vslot_next, tiles + ((t + 1) & 1) * BUF_ELEMS);
+      vslot_next = sring[(t + 2) & (SLOT_RING - 1)][lane];
       issue_slots(t + 3);
       compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0, nxt);
       lds_barrier();   // both key halves' probabilities are in LDS
+      // every write of restart_sh (in compute) precedes the barrier above
+      const uint32_t rs = restart_sh;
       value_pass(tiles + (t & 1) * BUF_ELEMS);
+      restart_seen = __builtin_amdgcn_readfirstlane(rs) != 0u;
     }
     vm_wait<0>();
     __syncthreads();   // all copies landed and all waves are done with the tiles
@@ -896,11 +919,27 @@ bool plan_ok(const va_plan* p) {
       p->rows_per_group != ROWS || p->tile_keys != TILE ||
       (p->mode != VA_MODE_FUSED && p->mode != VA_MODE_SPLIT_TREE))
     return false;
-  if (p->mode == VA_MODE_SPLIT_TREE) {
-    for (int r = 0; r < p->num_requests; ++r)
-      if (p->nsplit[r] < 2) return false;   // at least one prefix split + the tree block
+  // the derived tables must be the ones the planner writes: the kernels
+  // index through them without further checks
+  if (p->num_heads < 1 || p->work_begin[0] != 0 || p->tree_begin[0] != 0) return false;
+  const int min_ns = p->mode == VA_MODE_SPLIT_TREE ? 2 : 1;   // split: a prefix split + the tree block
+  for (int r = 0; r < p->num_requests; ++r) {
+    const int T = p->num_tree[r];
+    if (T < 1 || T > VA_MAX_TREE || p->tree_begin[r + 1] - p->tree_begin[r] != T) return false;
+    if (p->nsplit[r] < min_ns || p->nsplit[r] > VA_MAX_SPLITS) return false;
+    if (p->num_groups[r] != (T * p->num_heads + ROWS - 1) / ROWS) return false;
+    if ((int64_t)p->work_begin[r + 1] - p->work_begin[r] != (int64_t)p->nsplit[r] * p->num_groups[r])
+      return false;
   }
-  return true;
+  const int64_t work = p->total_work;
+  const int64_t o_bytes = align256(work * ROWS * DV * (int64_t)sizeof(uint16_t));
+  const int64_t lse_bytes = align256(work * ROWS * 2 * (int64_t)sizeof(float));
+  const int64_t st_bytes = align256(work * (int64_t)sizeof(uint32_t));
+  return p->work_begin[p->num_requests] == p->total_work &&
+         p->total_tree == p->tree_begin[p->num_requests] &&
+         (int64_t)p->total_rows == (int64_t)p->total_tree * p->num_heads &&
+         p->lse_offset == o_bytes && p->status_offset == o_bytes + lse_bytes &&
+         p->workspace_bytes == o_bytes + lse_bytes + st_bytes;
 }
 
 }  // namespace

@@ -153,6 +153,27 @@ def test_run_argument_errors_are_caught_before_launch():
                                        None) == 0
 
 
+@pytest.mark.parametrize("field,value", [("nsplit", 0), ("nsplit", 257), ("num_groups", 2),
+                                         ("work_begin", 5), ("num_tree", 65), ("total_work", 2),
+                                         ("workspace_bytes", 4096), ("lse_offset", 0),
+                                         ("num_heads", 0), ("total_rows", 1)])
+def test_tampered_plans_are_rejected_before_launch(field, value):
+    """The kernels index through the plan's derived tables; a plan that does
+    not satisfy the planner's invariants is refused (no launch, so no GPU)."""
+    lib = va.load_library()
+    plan = _plan(8, [100], [4])
+    bad = binding.VaPlan()
+    ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
+    f = getattr(bad, field)
+    if isinstance(f, int):
+        setattr(bad, field, value)
+    else:
+        f[1 if field == "work_begin" else 0] = value
+    assert _run(lib, bad, ws_bytes=1 << 30) == -5
+    assert lib.verify_attn_reduce(ctypes.byref(bad), _fake(1 << 20), _fake(4096), _fake(4096),
+                                  None) == -5
+
+
 @pytest.mark.parametrize("parent,ok", [([-1], True), ([-1, 0, 1, 0, -1], True), ([0], False),
                                        ([-1, 1], False), ([-1, -2], False), ([-1] * 65, False)])
 def test_check_tree(parent, ok):
