@@ -479,6 +479,11 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row, bool first,
                      const TileIssue& nxt) {
     const int kt = k0 + t * TILE;
+    // keep every Q fragment in an accumulation register for the whole loop:
+    // the score MFMAs read them there directly, where the allocator would
+    // otherwise copy most of them to VGPRs before each use
+#pragma unroll
+    for (int k = 0; k < QK_STEPS; ++k) asm volatile("" : "+a"(qf[k]));
     // S^T = K . Q^T for this wave's 32 keys over all 576 score columns
     f32x16 sacc;
 #pragma unroll
