@@ -719,7 +719,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       for (int qd = 0; qd < 4; ++qd) {
         const f16x4 h = {(_Float16)(o[cb][4 * qd] * scale), (_Float16)(o[cb][4 * qd + 1] * scale),
                          (_Float16)(o[cb][4 * qd + 2] * scale), (_Float16)(o[cb][4 * qd + 3] * scale)};
-        po[(cb * 4 + qd) * 64] = __builtin_bit_cast(u32x2, h);
+        // streaming stores: the partials are read once, by the merge, and
+        // leave no dirty lines for the end-of-kernel write-back
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h), &po[(cb * 4 + qd) * 64]);
       }
     }
     if (kh == 0 && lh == 0) {
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
       const int s = s0 + u * RED_WAVES;
       const bool in = s < ns;
       c[u] = in ? coef[s][prow] : 0.f;
-      v[u] = in ? src[(int64_t)s * split_step] : u32x2{0u, 0u};
+      v[u] = in ? __builtin_nontemporal_load(&src[(int64_t)s * split_step]) : u32x2{0u, 0u};   // read once
     }
 #pragma unroll
     for (int u = 0; u < RED_UNROLL; ++u) {
