@@ -186,6 +186,15 @@ __device__ __forceinline__ void dma16_v(uint32_t lds, const void* addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
                :: "s"(lds), "v"(addr) : "memory", "m0");
 }
+// the same two copies without the streaming hint, for data every block reads
+__device__ __forceinline__ void dma16_s_keep(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_v_keep(uint32_t lds, const void* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(addr) : "memory", "m0");
+}
 // 4 bytes per lane from a per-lane address (lane i writes lds + 4 i)
 __device__ __forceinline__ void dma4_v(uint32_t lds, const void* addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
@@ -364,6 +373,39 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     issue_slots(1);
   }
 
+  // ---- Q, all 576 score columns of the group's rows
+  const int rho = g * ROWS + rh * 32 + lrow;
+  const bool row_ok = rho < rows_r;
+  bf16x8 qf[QK_STEPS];
+  // The group's 64 Q rows are copied once into the second tile buffer, in
+  // the layout of a key tile (each row is read by the two key-half waves of
+  // its row half; one copy per block halves the Q traffic of loading the
+  // fragments per wave).  Rows past the group's end copy row 0 of the
+  // request: they repeat its scores exactly (so raise no restart of their
+  // own) and their partial rows are never merged.  Wave w copies rows
+  // 16w .. 16w+15.  The first tile goes into the first buffer; the second
+  // tile's copies start after the barrier at the top of the first tile,
+  // when every wave has read its fragments.
+  {
+    const uint16_t* const q0 = a.q + (int64_t)a.tree_begin[r] * H * DQK;
+    const int g0 = g * ROWS;
+    const uint32_t qbuf = lds_addr(tiles + BUF_ELEMS);
+#pragma unroll
+    for (int c = 0; c < LAT_DMA; ++c) {
+      const int i = wave * LAT_DMA + c;
+      const int rr = g0 + i < rows_r ? g0 + i : 0;
+      dma16_s_keep(qbuf + i * (LAT_STRIDE * 2), q0 + (int64_t)rr * DQK, lane * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < ROPE_DMA; ++j) {
+      const int kb = (wave * ROPE_DMA + j) * 8;
+      const int i = kb + (lane >> 3);
+      const int rr = g0 + i < rows_r ? g0 + i : 0;
+      dma16_v_keep(qbuf + (LAT_ELEMS + kb * DROPE) * 2,
+                   q0 + (int64_t)rr * DQK + DV + rope_piece(i, lane & 7) * 8);
+    }
+  }
+
   // ---- ancestor masks (bit j of anc[i]: draft node j is i or an ancestor of
   // i).  Lane i of wave 0 holds node i's parent; the chains are followed
   // through the wave, so the parent array is read once.
@@ -385,21 +427,6 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       }
     }
     anc[lane] = m;
-  }
-
-  // ---- Q fragments of this lane's row over all 576 score columns
-  const int rho = g * ROWS + rh * 32 + lrow;
-  const bool row_ok = rho < rows_r;
-  bf16x8 qf[QK_STEPS];
-  {
-    const int64_t qrow = (int64_t)a.tree_begin[r] * H + (row_ok ? rho : 0);
-    const uint16_t* qp = a.q + qrow * DQK + lh * 8;
-#pragma unroll
-    for (int k = 0; k < QK_STEPS; ++k) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qp + k * 16);
-      if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
-      qf[k] = __builtin_bit_cast(bf16x8, v);
-    }
   }
 
   // ---- tile loader.  For tile u, lane l takes the slot of key l from the
@@ -632,8 +659,18 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     // compiler-visible wait: also completes the Q loads, so the compiler adds
     // no wait of its own before their first use
     wait_vmcnt<0>();
-    __syncthreads();   // slots 0, 1, anc[], status_sh and restart_sh ready
+    __syncthreads();   // slots 0, 1, Q, anc[], status_sh and restart_sh ready
     if (pass == 0 && MODE != PREFIX) anc_row = row_ok ? anc[rho / H] : 0ull;
+    if (pass == 0) {
+      const uint16_t* const qb = tiles + BUF_ELEMS;
+      const int qr = rh * HALF + lrow;
+#pragma unroll
+      for (int k = 0; k < QK_STEPS; ++k) {
+        const int off = k < LAT_STEPS ? qr * LAT_STRIDE + lh * 8 + k * 16
+                                      : LAT_ELEMS + qr * DROPE + rope_piece(qr, 2 * (k - LAT_STEPS) + lh) * 8;
+        qf[k] = *reinterpret_cast<const bf16x8*>(qb + off);
+      }
+    }
     if (ntiles > 0) {
       const TileIssue first_tile = prepare_tile(0, sring[0][lane], tiles);
 #pragma unroll
