@@ -486,6 +486,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   // normalises the output, so the output is an exact weighted average of its
   // value rows.
   float m_ref = -INFINITY;
+  bf16x8 pown[2];   // this wave's own probabilities of the current tile (P operand)
   float m_seen = -INFINITY;
   float l_run = 0.f;
   float lb_run = 0.f;
@@ -590,46 +591,46 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
         pb[i] = bf16x2{(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
         lb_run = __builtin_amdgcn_fdot2_f32_bf16(pb[i], ones, lb_run, false);
       }
-      xp[rh][kh][ks][lane] = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, pb[0]),
-                                                              __builtin_bit_cast(uint32_t, pb[1]),
-                                                              __builtin_bit_cast(uint32_t, pb[2]),
-                                                              __builtin_bit_cast(uint32_t, pb[3])});
+      pown[ks] = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, pb[0]),
+                                                   __builtin_bit_cast(uint32_t, pb[1]),
+                                                   __builtin_bit_cast(uint32_t, pb[2]),
+                                                   __builtin_bit_cast(uint32_t, pb[3])});
+      xp[rh][kh][ks][lane] = pown[ks];
     }
   };
 
-  // O^T += V^T . P^T for this wave's 256 output columns over all 64 keys of
-  // the tile: 8 column blocks x 4 k-steps of 16 keys (k-steps 0,1 from key
-  // half 0, 2,3 from key half 1); V^T fragments by transpose reads.
-  auto value_pass = [&](const uint16_t* buf) {
-    // V^T fragments of column block cb, read one block ahead of its MFMAs
-    auto load_v = [&](bf16x8* vf, int cb) {
+  // O^T += V^T . P^T for this wave's 256 output columns over the 32 keys of
+  // key half `half` (value k-steps 2 half, 2 half + 1, P operand ph): 8
+  // column blocks x 2 k-steps, V^T fragments by transpose reads one block
+  // ahead.  Each tile runs it twice: first for the wave's own key half, whose
+  // probabilities are still in registers, while the other key-half wave
+  // finishes its scores; then, after the exchange barrier, for the other half.
+  auto value_half = [&](const uint16_t* buf, int half, const bf16x8* ph) {
+    auto load_v2 = [&](bf16x8* vf, int cb) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint16_t* p0 = buf + v_off + ks * 16 * LAT_STRIDE + cb * 32;
+      for (int j = 0; j < 2; ++j) {
+        const uint16_t* p0 = buf + v_off + (2 * half + j) * 16 * LAT_STRIDE + cb * 32;
         const i16x4 v0 = lds_read_tr16(p0);
         const i16x4 v1 = lds_read_tr16(p0 + 8 * LAT_STRIDE);
         const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        vf[ks] = __builtin_bit_cast(bf16x8, v8);
+        vf[j] = __builtin_bit_cast(bf16x8, v8);
       }
     };
-    bf16x8 pf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pf[ks] = xp[rh][ks >> 1][ks & 1][lane];
-    bf16x8 vfa[4], vfb[4];
-    load_v(vfa, 0);
+    bf16x8 vfa[2], vfb[2];
+    load_v2(vfa, 0);
 #pragma unroll
     for (int cb = 0; cb < O_HALF; cb += 2) {
-      load_v(vfb, cb + 1);
+      load_v2(vfb, cb + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfa[ks], pf[ks], o[cb], 0, 0, 0);
+      for (int j = 0; j < 2; ++j)
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfa[j], ph[j], o[cb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (cb + 2 < O_HALF) load_v(vfa, cb + 2);
+      if (cb + 2 < O_HALF) load_v2(vfa, cb + 2);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        o[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfb[ks], pf[ks], o[cb + 1], 0, 0, 0);
+      for (int j = 0; j < 2; ++j)
+        o[cb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfb[j], ph[j], o[cb + 1], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -696,10 +697,16 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       vslot_next = sring[(t + 2) & (SLOT_RING - 1)][lane];
       issue_slots(t + 3);
       compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0, nxt);
+      value_half(tiles + (t & 1) * BUF_ELEMS, kh, pown);
       lds_barrier();   // both key halves' probabilities are in LDS
       // every write of restart_sh (in compute) precedes the barrier above
       const uint32_t rs = restart_sh;
-      value_pass(tiles + (t & 1) * BUF_ELEMS);
+      {
+        bf16x8 poth[2];
+        poth[0] = xp[rh][kh ^ 1][0][lane];
+        poth[1] = xp[rh][kh ^ 1][1][lane];
+        value_half(tiles + (t & 1) * BUF_ELEMS, kh ^ 1, poth);
+      }
       restart_seen = __builtin_amdgcn_readfirstlane(rs) != 0u;
     }
     vm_wait<0>();
