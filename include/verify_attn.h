@@ -239,6 +239,17 @@ int verify_attn_gather_rows(const uint16_t* kv_pool, int64_t num_slots, int32_t 
                             const int32_t* slot_table, int32_t n, uint16_t* dst,
                             va_stream_t stream);
 
+/*
+ * verify_attn_stream_read - measurement helper: reads every 16-byte word of
+ * buf once with streaming loads (the device's plain read ceiling, against
+ * which the partial pass's effective bandwidth is compared) and XORs the
+ * XOR of all of buf's 32-bit words into *sink.  buf: `bytes` of device
+ * memory, 16-byte aligned, bytes a multiple of 16.  sink: one device uint32
+ * the caller initialises.  Enqueue only; allocates nothing.
+ * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_ALIGN, VA_ERR_HIP.
+ */
+int verify_attn_stream_read(const void* buf, int64_t bytes, uint32_t* sink, va_stream_t stream);
+
 /* Static text for a return code. */
 const char* verify_attn_error_string(int code);
 

@@ -39,7 +39,8 @@ STATUS_BITS = {1: "BAD_PREFIX", 2: "SHORT_TABLE", 4: "BAD_SLOT", 8: "BAD_PARENT"
 EXPORTS = (
     "verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
     "verify_attn_read_status",
-    "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_error_string",
+    "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_stream_read",
+    "verify_attn_error_string",
     "verify_attn_plan_struct_size", "verify_attn_compact_workspace_bytes", "verify_attn_compact",
     "verify_attn_build_tree",
 )
@@ -101,6 +102,7 @@ def load_library(path: os.PathLike | None = None):
                                             ctypes.POINTER(ctypes.c_uint32)]
     lib.verify_attn_check_tree.argtypes = [P, i32]
     lib.verify_attn_gather_rows.argtypes = [P, i64, i32, P, i32, P, P]
+    lib.verify_attn_stream_read.argtypes = [P, i64, P, P]
     lib.verify_attn_error_string.argtypes = [ctypes.c_int]
     lib.verify_attn_error_string.restype = ctypes.c_char_p
     lib.verify_attn_compact_workspace_bytes.argtypes = [i32, i32]
@@ -112,7 +114,8 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_plan_struct_size.argtypes = []
     lib.verify_attn_plan_struct_size.restype = sz
     for name in ("verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
-                 "verify_attn_read_status", "verify_attn_check_tree", "verify_attn_gather_rows"):
+                 "verify_attn_read_status", "verify_attn_check_tree", "verify_attn_gather_rows",
+                 "verify_attn_stream_read"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.verify_attn_plan_struct_size() != ctypes.sizeof(VaPlan):
         raise RuntimeError("va_plan layout mismatch between library and binding")
@@ -245,6 +248,22 @@ def verify_attn_gather_rows(kv_pool, slot_table, n, dst, stream=None):
         _dptr(slot_table, (torch.int32,), "slot_table"), int(n),
         _dptr(dst, _bf16_types(), "dst"), _stream_handle(stream))
     _check("verify_attn_gather_rows", rc)
+
+
+def verify_attn_stream_read(buf, sink, stream=None):
+    """Read every byte of the device tensor `buf` once (the read-ceiling
+    helper); XORs the XOR of its 32-bit words into the int32 device tensor
+    `sink` (one element, initialised by the caller)."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink.numel() < 1 or sink.dtype != torch.int32 or not sink.is_cuda:
+        raise ValueError("sink must be a device int32 tensor")
+    nbytes = buf.numel() * buf.element_size()
+    rc = load_library().verify_attn_stream_read(ctypes.c_void_p(buf.data_ptr()), int(nbytes),
+                                                ctypes.c_void_p(sink.data_ptr()),
+                                                _stream_handle(stream))
+    _check("verify_attn_stream_read", rc)
 
 
 def verify_attn_error_string(code) -> str:

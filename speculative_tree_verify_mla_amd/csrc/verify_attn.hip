@@ -913,6 +913,38 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   }
 }
 
+// Measurement helper: the read ceiling the partial pass is compared with.
+// Every 16-byte word of buf is read once (streaming loads, four in flight
+// per thread); the XOR of all its 32-bit words is folded into *sink, so the
+// reads cannot be dropped and a test can check that each word was read
+// exactly once.
+constexpr int STREAM_THREADS = 256;
+constexpr int STREAM_BLOCKS_PER_CU = 8;
+__global__ __launch_bounds__(STREAM_THREADS) void va_stream_read_kernel(const u32x4* buf, int64_t n16,
+                                                                          uint32_t* sink) {
+  __shared__ uint32_t part[STREAM_THREADS / 64];
+  const int64_t stride = (int64_t)gridDim.x * STREAM_THREADS;
+  int64_t i = (int64_t)blockIdx.x * STREAM_THREADS + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(buf + i);
+    const u32x4 b = __builtin_nontemporal_load(buf + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(buf + i);
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0u;
+    for (int w = 0; w < STREAM_THREADS / 64; ++w) t ^= part[w];
+    atomicXor(sink, t);
+  }
+}
+
 // Diagnostic: pool rows through the partial pass's table/slot checks and its
 // 16-byte global->LDS copy; one block of 64 threads per row.
 __global__ __launch_bounds__(64) void va_gather_kernel(const uint16_t* kv, int64_t num_slots,
@@ -1217,6 +1249,22 @@ int verify_attn_gather_rows(const uint16_t* kv_pool, int64_t num_slots, int32_t 
   hipLaunchKernelGGL(va_gather_kernel, dim3((unsigned)n), dim3(64), 0,
                      static_cast<hipStream_t>(stream), kv_pool, num_slots, kv_row_stride,
                      slot_table, n, dst);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+int verify_attn_stream_read(const void* buf, int64_t bytes, uint32_t* sink, va_stream_t stream) {
+  if (buf == nullptr || sink == nullptr) return VA_ERR_NULL;
+  if (bytes < 0 || (bytes & 15) != 0) return VA_ERR_SHAPE;
+  if (!aligned16(buf)) return VA_ERR_ALIGN;
+  if (bytes == 0) return VA_OK;
+  int32_t cus = 0;
+  const int rc = query_num_cus(&cus);
+  if (rc != VA_OK) return rc;
+  const int64_t n16 = bytes / 16;
+  const int64_t want = (n16 + STREAM_THREADS - 1) / STREAM_THREADS;
+  const unsigned blocks = (unsigned)std::min<int64_t>(want, (int64_t)cus * STREAM_BLOCKS_PER_CU);
+  hipLaunchKernelGGL(va_stream_read_kernel, dim3(blocks), dim3(STREAM_THREADS), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), n16, sink);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
