@@ -366,7 +366,7 @@ def main():
         # measured read ceiling of this GPU: the library's streaming-read
         # helper over 2 GiB (every word read once), best of 5 passes
         big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
-        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        sink = torch.zeros(4096, dtype=torch.int32, device=dev)
         best = None
         with torch.cuda.stream(stream):
             va.verify_attn_stream_read(big, sink, stream)

@@ -242,13 +242,17 @@ int verify_attn_gather_rows(const uint16_t* kv_pool, int64_t num_slots, int32_t 
 /*
  * verify_attn_stream_read - measurement helper: reads every 16-byte word of
  * buf once with streaming loads (the device's plain read ceiling, against
- * which the partial pass's effective bandwidth is compared) and XORs the
- * XOR of all of buf's 32-bit words into *sink.  buf: `bytes` of device
- * memory, 16-byte aligned, bytes a multiple of 16.  sink: one device uint32
- * the caller initialises.  Enqueue only; allocates nothing.
+ * which the partial pass's effective bandwidth is compared).  Each of its
+ * blocks XORs the XOR of the 32-bit words it read into one of the
+ * sink_words words of sink, so the XOR of all sink words (which the caller
+ * initialises) equals the XOR of buf's words.  Up to 8 blocks per compute
+ * unit; with sink_words at least that many no two blocks share a word.
+ * buf: `bytes` of device memory, 16-byte aligned, bytes a multiple of 16.
+ * sink: sink_words >= 1 device uint32.  Enqueue only; allocates nothing.
  * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_ALIGN, VA_ERR_HIP.
  */
-int verify_attn_stream_read(const void* buf, int64_t bytes, uint32_t* sink, va_stream_t stream);
+int verify_attn_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t sink_words,
+                            va_stream_t stream);
 
 /* Static text for a return code. */
 const char* verify_attn_error_string(int code);

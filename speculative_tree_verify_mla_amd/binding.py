@@ -102,7 +102,7 @@ def load_library(path: os.PathLike | None = None):
                                             ctypes.POINTER(ctypes.c_uint32)]
     lib.verify_attn_check_tree.argtypes = [P, i32]
     lib.verify_attn_gather_rows.argtypes = [P, i64, i32, P, i32, P, P]
-    lib.verify_attn_stream_read.argtypes = [P, i64, P, P]
+    lib.verify_attn_stream_read.argtypes = [P, i64, P, i32, P]
     lib.verify_attn_error_string.argtypes = [ctypes.c_int]
     lib.verify_attn_error_string.restype = ctypes.c_char_p
     lib.verify_attn_compact_workspace_bytes.argtypes = [i32, i32]
@@ -252,8 +252,9 @@ def verify_attn_gather_rows(kv_pool, slot_table, n, dst, stream=None):
 
 def verify_attn_stream_read(buf, sink, stream=None):
     """Read every byte of the device tensor `buf` once (the read-ceiling
-    helper); XORs the XOR of its 32-bit words into the int32 device tensor
-    `sink` (one element, initialised by the caller)."""
+    helper); the XOR of all words of the int32 device tensor `sink`
+    (initialised by the caller; 4096 words keep blocks from sharing one)
+    becomes the XOR of buf's 32-bit words."""
     import torch
     if not buf.is_cuda or not buf.is_contiguous():
         raise ValueError("buf must be a contiguous device tensor")
@@ -261,7 +262,7 @@ def verify_attn_stream_read(buf, sink, stream=None):
         raise ValueError("sink must be a device int32 tensor")
     nbytes = buf.numel() * buf.element_size()
     rc = load_library().verify_attn_stream_read(ctypes.c_void_p(buf.data_ptr()), int(nbytes),
-                                                ctypes.c_void_p(sink.data_ptr()),
+                                                ctypes.c_void_p(sink.data_ptr()), int(sink.numel()),
                                                 _stream_handle(stream))
     _check("verify_attn_stream_read", rc)
 

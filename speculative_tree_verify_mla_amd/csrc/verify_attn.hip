@@ -782,22 +782,28 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
 
 // Log-sum-exp merge of the splits.  One block of 512 threads per (request,
 // row group, row half, 32-column block, 4-column quad):
-// 32 rows x 8 columns, read as one contiguous 512-byte piece per split.  The
-// threads first turn each split's (lse, scale exponent e) into the
-// coefficient exp2(lse_s - max) * 2^e_s of every row; then the 8 waves each
-// accumulate an eighth of the splits, 8 independent 512-byte loads at a
-// time, and add up through LDS.
+// 32 rows x 8 columns, read as one contiguous 512-byte piece per split.
+// All of the block's loads go out together, so the merge costs one memory
+// round trip: thread (split group sg, row) loads the (lse, scale exponent e)
+// pairs of splits sg, sg + 16, ..., wave v the pieces of splits v, v + 8,
+// ..., and thread i the status word of split i.  Loads past the request's
+// last split re-read that split (in bounds, no branch around any load) and
+// are dropped.  Then, on registers and LDS: the row max over the splits, the
+// coefficients exp2(lse_s - max) * 2^e_s, each wave's weighted sum of its
+// pieces, and the sum over the waves.
 constexpr int RED_THREADS = 512;
 constexpr int RED_WAVES = RED_THREADS / 64;
-constexpr int RED_SG = RED_THREADS / 32;      // split groups of the coefficient pass
-constexpr int RED_UNROLL = 8;
+constexpr int RED_SG = RED_THREADS / 32;    // split groups of the lse loads
 constexpr int RED_PIECES = 2 * O_BLK * 4;   // blocks per row group
 
+// MAXS: a bound on every request's split count, a multiple of RED_SG
+template <int MAXS>
 __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
-  __shared__ float coef[VA_MAX_SPLITS][32];
+  constexpr int RED_LSE = MAXS / RED_SG;           // lse pairs per thread
+  constexpr int RED_PER_WAVE = MAXS / RED_WAVES;   // pieces per lane
+  __shared__ float coef[MAXS][32];
   __shared__ float red_m[RED_SG][32];
   __shared__ float red_w[RED_SG][32];
-  __shared__ uint32_t red_s[RED_SG][32];
   __shared__ f32x4 part[RED_WAVES][64];
 
   const int tid = threadIdx.x;
@@ -821,57 +827,53 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   const int rows_r = (a.tree_begin[r + 1] - a.tree_begin[r]) * H;
   const int64_t wbase = (int64_t)a.work_begin[r] + g;   // work item of split s: wbase + s * G
 
-  // per-row max and weight sums over the splits: thread = (split group sg, row)
   const int row = tid & 31;
   const int sg = tid >> 5;
+  const int prow = lane & 31;
   const float2* plse = reinterpret_cast<const float2*>(a.part_lse) + wbase * ROWS + rh * 32 + row;
+  const u32x2* src = reinterpret_cast<const u32x2*>(a.part_o) + wbase * PART_VEC + piece * 64 + lane;
+  const int64_t lse_step = (int64_t)G * ROWS;
+  const int64_t split_step = (int64_t)G * PART_VEC;
+  float2 lv[RED_LSE];
+#pragma unroll
+  for (int i = 0; i < RED_LSE; ++i) lv[i] = plse[min(sg + i * RED_SG, ns - 1) * lse_step];
+  u32x2 v[RED_PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < RED_PER_WAVE; ++u)
+    v[u] = __builtin_nontemporal_load(&src[min(wave + u * RED_WAVES, ns - 1) * split_step]);   // read once
+  const uint32_t st = a.status[wbase + (int64_t)min(tid, ns - 1) * G];
+
+  // per-row max over the splits
   float m = -INFINITY;
-  uint32_t st = 0u;
-#pragma unroll 4
-  for (int s = sg; s < ns; s += RED_SG) {
-    const int64_t w = wbase + (int64_t)s * G;
-    m = fmaxf(m, plse[(int64_t)s * G * ROWS].x);
-    st |= a.status[w];
-  }
+#pragma unroll
+  for (int i = 0; i < RED_LSE; ++i) m = sg + i * RED_SG < ns ? fmaxf(m, lv[i].x) : m;
   red_m[sg][row] = m;
-  red_s[sg][row] = st;
-  __syncthreads();
+  const int any_bad = __syncthreads_or(st != 0u);
   float M = red_m[0][row];
 #pragma unroll
   for (int i = 1; i < RED_SG; ++i) M = fmaxf(M, red_m[i][row]);
+  // coefficients and weight sums
   float wsum = 0.f;
-#pragma unroll 4
-  for (int s = sg; s < ns; s += RED_SG) {
-    const float2 v = plse[(int64_t)s * G * ROWS];
-    const float e = (v.x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(v.x - M);
+#pragma unroll
+  for (int i = 0; i < RED_LSE; ++i) {
+    const int s = sg + i * RED_SG;
+    const float e = (s >= ns || lv[i].x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(lv[i].x - M);
     wsum += e;
-    coef[s][row] = e > 0.f ? ldexpf(e, (int)v.y) : 0.f;
+    if (s < ns) coef[s][row] = e > 0.f ? ldexpf(e, (int)lv[i].y) : 0.f;
   }
   red_w[sg][row] = wsum;
   __syncthreads();
 
-  // weighted sum of this block's 1 KB piece over the splits (a split whose
-  // coefficient is 0 adds nothing, whatever its partial holds)
-  const int prow = lane & 31;
+  // weighted sum of this wave's pieces (a split whose coefficient is 0 adds
+  // nothing, whatever its partial holds)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const u32x2* src = reinterpret_cast<const u32x2*>(a.part_o) + wbase * PART_VEC + piece * 64 + lane;
-  const int64_t split_step = (int64_t)G * PART_VEC;
-  for (int s0 = wave; s0 < ns; s0 += RED_WAVES * RED_UNROLL) {
-    u32x2 v[RED_UNROLL];
-    float c[RED_UNROLL];
 #pragma unroll
-    for (int u = 0; u < RED_UNROLL; ++u) {
-      const int s = s0 + u * RED_WAVES;
-      const bool in = s < ns;
-      c[u] = in ? coef[s][prow] : 0.f;
-      v[u] = in ? __builtin_nontemporal_load(&src[(int64_t)s * split_step]) : u32x2{0u, 0u};   // read once
-    }
-#pragma unroll
-    for (int u = 0; u < RED_UNROLL; ++u) {
-      const f16x4 h = __builtin_bit_cast(f16x4, v[u]);
-      const f32x4 x = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-      if (c[u] != 0.f) acc += c[u] * x;
-    }
+  for (int u = 0; u < RED_PER_WAVE; ++u) {
+    const int s = wave + u * RED_WAVES;
+    const float c = s < ns ? coef[s][prow] : 0.f;
+    const f16x4 h = __builtin_bit_cast(f16x4, v[u]);
+    const f32x4 x = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    if (c != 0.f) acc += c * x;
   }
   part[wave][lane] = acc;
   __syncthreads();
@@ -880,12 +882,11 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (int i = 1; i < RED_WAVES; ++i) tot += part[i][lane];
     float W = 0.f;
-    uint32_t Sr = 0u;
+    const uint32_t Sr = any_bad ? 1u : 0u;
     float Mr = red_m[0][prow];
 #pragma unroll
     for (int i = 0; i < RED_SG; ++i) {
       W += red_w[i][prow];
-      Sr |= red_s[i][prow];
       Mr = fmaxf(Mr, red_m[i][prow]);
     }
     const int rr = g * ROWS + rh * 32 + prow;   // row within the request
@@ -915,13 +916,14 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
 
 // Measurement helper: the read ceiling the partial pass is compared with.
 // Every 16-byte word of buf is read once (streaming loads, four in flight
-// per thread); the XOR of all its 32-bit words is folded into *sink, so the
-// reads cannot be dropped and a test can check that each word was read
-// exactly once.
+// per thread); block b folds the XOR of the 32-bit words it read into
+// sink[b % sink_words], so the reads cannot be dropped and a test can check
+// that each word was read exactly once.  With sink_words at least the grid
+// size no two blocks share a sink word (atomics on one word serialise).
 constexpr int STREAM_THREADS = 256;
 constexpr int STREAM_BLOCKS_PER_CU = 8;
 __global__ __launch_bounds__(STREAM_THREADS) void va_stream_read_kernel(const u32x4* buf, int64_t n16,
-                                                                          uint32_t* sink) {
+                                                                          uint32_t* sink, int sink_words) {
   __shared__ uint32_t part[STREAM_THREADS / 64];
   const int64_t stride = (int64_t)gridDim.x * STREAM_THREADS;
   int64_t i = (int64_t)blockIdx.x * STREAM_THREADS + threadIdx.x;
@@ -941,7 +943,7 @@ __global__ __launch_bounds__(STREAM_THREADS) void va_stream_read_kernel(const u3
   if (threadIdx.x == 0) {
     uint32_t t = 0u;
     for (int w = 0; w < STREAM_THREADS / 64; ++w) t ^= part[w];
-    atomicXor(sink, t);
+    atomicXor(sink + blockIdx.x % sink_words, t);
   }
 }
 
@@ -1203,9 +1205,22 @@ int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out
     a.work_begin[r] = plan->work_begin[r];
   }
   int blocks = 0;
-  for (int r = 0; r < plan->num_requests; ++r) blocks += plan->num_groups[r] * RED_PIECES;
-  hipLaunchKernelGGL(va_reduce_kernel, dim3(blocks), dim3(RED_THREADS), 0,
-                     static_cast<hipStream_t>(stream), a);
+  int max_ns = 1;
+  for (int r = 0; r < plan->num_requests; ++r) {
+    blocks += plan->num_groups[r] * RED_PIECES;
+    max_ns = max(max_ns, plan->nsplit[r]);
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (max_ns <= 16)
+    hipLaunchKernelGGL(va_reduce_kernel<16>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else if (max_ns <= 32)
+    hipLaunchKernelGGL(va_reduce_kernel<32>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else if (max_ns <= 64)
+    hipLaunchKernelGGL(va_reduce_kernel<64>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else if (max_ns <= 128)
+    hipLaunchKernelGGL(va_reduce_kernel<128>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(va_reduce_kernel<VA_MAX_SPLITS>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
@@ -1252,9 +1267,10 @@ int verify_attn_gather_rows(const uint16_t* kv_pool, int64_t num_slots, int32_t 
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
-int verify_attn_stream_read(const void* buf, int64_t bytes, uint32_t* sink, va_stream_t stream) {
+int verify_attn_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t sink_words,
+                            va_stream_t stream) {
   if (buf == nullptr || sink == nullptr) return VA_ERR_NULL;
-  if (bytes < 0 || (bytes & 15) != 0) return VA_ERR_SHAPE;
+  if (bytes < 0 || (bytes & 15) != 0 || sink_words < 1) return VA_ERR_SHAPE;
   if (!aligned16(buf)) return VA_ERR_ALIGN;
   if (bytes == 0) return VA_OK;
   int32_t cus = 0;
@@ -1264,7 +1280,8 @@ int verify_attn_stream_read(const void* buf, int64_t bytes, uint32_t* sink, va_s
   const int64_t want = (n16 + STREAM_THREADS - 1) / STREAM_THREADS;
   const unsigned blocks = (unsigned)std::min<int64_t>(want, (int64_t)cus * STREAM_BLOCKS_PER_CU);
   hipLaunchKernelGGL(va_stream_read_kernel, dim3(blocks), dim3(STREAM_THREADS), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), n16, sink);
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), n16, sink,
+                     sink_words);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 

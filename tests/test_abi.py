@@ -152,12 +152,13 @@ def test_run_argument_errors_are_caught_before_launch():
     assert lib.verify_attn_gather_rows(_fake(4096), 10, 576, _fake(64), 0, _fake(4096),
                                        None) == 0
     # the read-ceiling helper: checks before any launch; 0 bytes launches nothing
-    assert lib.verify_attn_stream_read(None, 1024, _fake(4096), None) == -1
-    assert lib.verify_attn_stream_read(_fake(4096), 1024, None, None) == -1
-    assert lib.verify_attn_stream_read(_fake(4096), 1000, _fake(4096), None) == -2
-    assert lib.verify_attn_stream_read(_fake(4096), -16, _fake(4096), None) == -2
-    assert lib.verify_attn_stream_read(_fake(4104), 1024, _fake(4096), None) == -3
-    assert lib.verify_attn_stream_read(_fake(4096), 0, _fake(4096), None) == 0
+    assert lib.verify_attn_stream_read(None, 1024, _fake(4096), 1, None) == -1
+    assert lib.verify_attn_stream_read(_fake(4096), 1024, None, 1, None) == -1
+    assert lib.verify_attn_stream_read(_fake(4096), 1000, _fake(4096), 1, None) == -2
+    assert lib.verify_attn_stream_read(_fake(4096), -16, _fake(4096), 1, None) == -2
+    assert lib.verify_attn_stream_read(_fake(4096), 1024, _fake(4096), 0, None) == -2
+    assert lib.verify_attn_stream_read(_fake(4104), 1024, _fake(4096), 1, None) == -3
+    assert lib.verify_attn_stream_read(_fake(4096), 0, _fake(4096), 1, None) == 0
 
 
 @pytest.mark.parametrize("field,value", [("nsplit", 0), ("nsplit", 257), ("num_groups", 2),

@@ -11,15 +11,16 @@ from test_parity import DEV, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("nbytes", [16, 4096, (1 << 20) + 48, 37 * (1 << 20) + 16 * 7])
-def test_every_word_read_once(nbytes):
+@pytest.mark.parametrize("nbytes,words", [(16, 1), (4096, 1), ((1 << 20) + 48, 4096),
+                                          (37 * (1 << 20) + 16 * 7, 4096), (37 * (1 << 20) + 16 * 7, 3)])
+def test_every_word_read_once(nbytes, words):
     rng = np.random.default_rng(nbytes)
     host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
     buf = torch.from_numpy(host.view(np.int32)).to(DEV)
-    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(words, dtype=torch.int32, device=DEV)
     va.verify_attn_stream_read(buf, sink)
     torch.cuda.synchronize()
     want = int(np.bitwise_xor.reduce(host))
-    got = int(sink.cpu().numpy().view(np.uint32)[0])
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
     say(f"  stream read {nbytes} B: xor {got:#010x} (expected {want:#010x})")
     assert got == want
