@@ -30,6 +30,7 @@ namespace {
 constexpr int CB = 1024;           // table entries per block of the count/select passes
 constexpr int ROW_PIECES = VA_D_QK * 2 / 16;   // 72 pieces of 16 bytes per row
 constexpr int COPY_THREADS = 256;
+typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
 
 struct CompactArgs {
   uint16_t* kv;
@@ -166,8 +167,9 @@ __global__ __launch_bounds__(COPY_THREADS) void compact_copy_kernel(CompactArgs 
   const int32_t k = a.sel_pos[i];
   const int64_t src = a.sel_src[i];
   const int64_t dst = (int64_t)a.dst_begin + k;
-  const uint4 v = *reinterpret_cast<const uint4*>(a.kv + src * a.stride + p * 8);
-  *reinterpret_cast<uint4*>(a.kv + dst * a.stride + p * 8) = v;
+  // streaming: each source row is read once and each destination written once
+  const vec4u v = __builtin_nontemporal_load(reinterpret_cast<const vec4u*>(a.kv + src * a.stride + p * 8));
+  __builtin_nontemporal_store(v, reinterpret_cast<vec4u*>(a.kv + dst * a.stride + p * 8));
   if (p == 0) a.table[k] = (int32_t)dst;
 }
 
