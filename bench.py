@@ -46,8 +46,13 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_va_partial_kernel_tp_r
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the kernel source's code: line comments, trailing blanks and
+    empty lines removed, so a comment edit keeps a measurement valid while
+    any code change voids it (the source has no block comments and no "//"
+    inside string literals)."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        lines = [ln.split("//", 1)[0].rstrip() for ln in f]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
 def traffic_from_profile():

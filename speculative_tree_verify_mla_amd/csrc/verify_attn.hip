@@ -15,11 +15,15 @@
 //   - 256 threads = 4 wave64s, one per SIMD.  Wave w owns row half
 //     rh = w & 1 (32 query rows, the MFMA N dimension) and half kh = w >> 1
 //     of the work: for the score, keys 32*kh .. +31 of every 64-key tile over
-//     all 576 columns (the full Q of its rows stays in VGPRs, so no partial
-//     scores are exchanged); for the output, columns 256*kh .. +255 over all
-//     64 keys.  The two key halves hand each other their bf16 probabilities
-//     through an 8 KB LDS buffer: one barrier per tile besides the tile
-//     barrier.
+//     all 576 columns (the full Q of its rows stays in accumulation
+//     registers, so no partial scores are exchanged); for the output, columns
+//     256*kh .. +255 over all 64 keys.  The two key halves hand each other
+//     their bf16 probabilities through an 8 KB LDS buffer: one barrier per
+//     tile besides the tile barrier.  Each wave runs the output MFMAs of its
+//     own key half before that barrier and the other half's after it.
+//   - The group's Q rows are copied once into the second tile buffer in the
+//     tile layout, each wave reads its fragments from there, and the first
+//     tile's barrier frees the buffer for the second tile.
 //   - Tiles of 64 pool rows go straight from HBM into LDS with
 //     global_load_lds_dwordx4 (1 KB per wave instruction), double-buffered:
 //     one tile is in flight while the other is consumed.  The slot-table
@@ -30,7 +34,7 @@
 //     XOR-swizzled, so both MFMA read patterns below are free of LDS bank
 //     conflicts.
 //   - S^T[key][row] = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K fragment
-//     from LDS, B = Q rows held in VGPRs).  The output layout gives each lane
+//     from LDS, B = Q rows held in accumulation registers).  The output layout gives each lane
 //     one query row (lane % 32) and, per register quad, 4 of the wave's keys,
 //     so the probabilities of keys 16*ks .. +15 are, register for register,
 //     the B operand of O^T = V^T . P^T for k-step ks.  That operand's A side
@@ -47,8 +51,9 @@
 //     prologue from parent[]; only tiles reaching past the prefix consult it.
 //   - Each work item writes its normalised output o / lb (lb = the sum of the
 //     bf16 weights) in fp16 with a per-row power-of-two scale, in the MFMA
-//     output layout (512 B per wave store), and its lse (base 2); the reduce
-//     merges a row's splits and writes bf16 out and natural-log lse.
+//     output layout (512 B per wave store, streaming stores: only the merge
+//     reads them), and its lse (base 2); the reduce merges a row's splits
+//     with one round of loads and writes bf16 out and natural-log lse.
 
 #include <hip/hip_runtime.h>
 // m0 is set inside the copy asm (nothing else in these kernels uses it)
