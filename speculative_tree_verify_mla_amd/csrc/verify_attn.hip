@@ -59,6 +59,7 @@
 // m0 is set inside the copy asm (nothing else in these kernels uses it)
 #pragma clang diagnostic ignored "-Winline-asm"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -87,7 +88,7 @@ constexpr int PART_VEC = ROWS * DV / 4;  // 4-column entries of one work item's 
 constexpr int SLOT_RING = 4;         // LDS ring of per-tile slot-table entries (3 live)
 constexpr int LAT_DMA = TILE / 4;    // latent rows one wave copies per tile
 constexpr int ROPE_DMA = TILE / 32;  // rope blocks (8 keys each) one wave copies per tile
-constexpr int MIN_KEYS_PER_SPLIT = 256;
+constexpr int MIN_KEYS_PER_SPLIT = 128;
 constexpr float REF_SLACK = 64.f;  // log2 units: probabilities stay <= 2^64
 constexpr int MAX_PASSES = 8;      // restarts of a work item with a raised reference
 constexpr float LOG2E = 1.4426950408889634f;
@@ -1086,21 +1087,42 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   if (keys_per_item < MIN_KEYS_PER_SPLIT) keys_per_item = MIN_KEYS_PER_SPLIT;
   int forced = 0;
   if (const char* e = std::getenv("VA_NSPLIT")) forced = std::atoi(e);
+  // prefix split count of request r for a given split length
+  auto nsplit_of = [&](int r, int64_t kpi) -> int64_t {
+    const int64_t n = (int64_t)h_prefix_len[r] + (split_tree ? 0 : h_num_tree[r]);
+    int64_t ns = forced > 0 ? forced : (n + kpi - 1) / kpi;
+    const int64_t max_ns = (n + SPLIT_ALIGN - 1) / SPLIT_ALIGN;
+    const int64_t cap = split_tree ? VA_MAX_SPLITS - 1 : VA_MAX_SPLITS;
+    if (ns > max_ns) ns = max_ns;
+    if (ns > cap) ns = cap;
+    return ns < 1 ? 1 : ns;
+  };
+  // Each request's split count is rounded up, so the work items can add up to
+  // more than the CUs, and the blocks past them would run as a second round
+  // on the machine, doubling the call.  Lengthen the splits until the items
+  // fit (or every request is down to one split per row group).
+  if (forced == 0) {
+    for (;;) {
+      int64_t items = 0;
+      bool more = false;
+      for (int r = 0; r < num_requests; ++r) {
+        const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
+        const int64_t ns = nsplit_of(r, keys_per_item);
+        items += groups * ns;
+        more |= ns > 1;
+      }
+      if (items <= cus || !more) break;
+      keys_per_item += std::max<int64_t>(SPLIT_ALIGN, keys_per_item / 64);
+    }
+  }
 
   int64_t work = 0;
   int64_t tree = 0;
   p.tree_begin[0] = 0;
   p.work_begin[0] = 0;
   for (int r = 0; r < num_requests; ++r) {
-    // keys the (prefix) splits share
-    const int64_t n = (int64_t)h_prefix_len[r] + (split_tree ? 0 : h_num_tree[r]);
     const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
-    int64_t ns = forced > 0 ? forced : (n + keys_per_item - 1) / keys_per_item;
-    const int64_t max_ns = (n + SPLIT_ALIGN - 1) / SPLIT_ALIGN;
-    const int64_t cap = split_tree ? VA_MAX_SPLITS - 1 : VA_MAX_SPLITS;
-    if (ns > max_ns) ns = max_ns;
-    if (ns > cap) ns = cap;
-    if (ns < 1) ns = 1;
+    int64_t ns = nsplit_of(r, keys_per_item);
     if (split_tree) ns += 1;   // the tree block
     p.num_tree[r] = h_num_tree[r];
     p.max_prefix[r] = h_prefix_len[r];

@@ -70,14 +70,21 @@ def test_plan_full_heads_and_ragged_batch():
     assert [p.num_groups[r] for r in range(4)] == [8] * 4
     keys = [1024 + 32, 16384 + 32, 65536 + 32, 131072 + 32]
     per = -(-8 * sum(keys) // 256)
-    assert p.splits() == [-(-k // per) for k in keys]
-    assert p.work_begin[4] == p.total_work == 8 * sum(p.splits())
+    # the first split length rounds up to [1, 3, 10, 20] = 272 items for 256
+    # CUs; splits are lengthened (by max(32, per / 64) keys a step) until the
+    # items fit
+    while 8 * sum(-(-k // per) for k in keys) > 256:
+        per += max(32, per // 64)
+    assert p.splits() == [-(-k // per) for k in keys] == [1, 3, 9, 18]
+    assert p.work_begin[4] == p.total_work == 8 * sum(p.splits()) == 248
     assert [p.tree_begin[r] for r in range(5)] == [0, 32, 64, 96, 128]
 
 
 def test_plan_small_inputs_keep_a_minimum_split_length():
     p = _plan(8, [256], [4])
-    assert p.num_groups[0] == 1 and p.nsplit[0] == 2      # 260 keys, >= 256 per split
+    assert p.num_groups[0] == 1 and p.nsplit[0] == 3      # 260 keys, >= 128 per split
+    p = _plan(8, [4096], [16])
+    assert p.num_groups[0] == 2 and p.nsplit[0] == 33     # 4112 keys in splits of >= 128
     p = _plan(1, [0], [1])
     assert p.nsplit[0] == 1 and p.total_work == 1 and p.total_rows == 1
 
@@ -238,3 +245,26 @@ def test_plan_ex_rejects_unknown_flags_and_bad_modes():
     bad.mode = binding.VA_MODE_SPLIT_TREE           # a split-tree plan needs >= 2 splits
     bad.nsplit[0] = 1
     assert _run(lib, bad) == -5
+
+
+@pytest.mark.parametrize("split_tree", [False, True])
+def test_plans_fit_the_compute_units(split_tree):
+    """Rounded-up split counts must not add up to more work items than CUs
+    (the excess would run as a second round of blocks), unless every request
+    is already down to one split per row group."""
+    rng = np.random.default_rng(7)
+    cases = [(16, [1024, 16384, 65536, 131072], [32] * 4, 256), (8, [65536], [16], 256),
+             (64, [200000], [16], 256), (8, [4096], [16], 256), (16, [1024, 16384, 65536, 131072], [32] * 4, 80)]
+    for _ in range(40):
+        B = int(rng.integers(1, 9))
+        cases.append((int(rng.integers(1, 65)), [int(x) for x in rng.integers(0, 300000, B)],
+                      [int(x) for x in rng.integers(1, 65, B)], int(rng.choice([32, 100, 256, 304]))))
+    for H, L, T, cus in cases:
+        p = va.verify_attn_plan(H, L, T, num_cus=cus, split_tree=split_tree)
+        groups = [(t * H + 63) // 64 for t in T]
+        ns = list(p.nsplit[:len(L)])
+        prefix_splits = [n - 1 for n in ns] if split_tree else ns
+        budget = cus - (sum(groups) if split_tree else 0)
+        prefix_items = sum(g * n for g, n in zip(groups, prefix_splits))
+        assert prefix_items <= max(budget, 1) or all(n == 1 for n in prefix_splits), (H, L, T, cus, ns)
+        assert p.total_work == sum(g * n for g, n in zip(groups, ns))
