@@ -1083,7 +1083,12 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
     if (split_tree) cus -= groups;   // compute units the tree-block work items occupy
   }
   if (cus < 1) cus = 1;
-  int64_t keys_per_item = (units + cus - 1) / cus;
+  // A work item takes ceil(keys / TILE) tile iterations whatever the keys in
+  // its last tile, so the split length is rounded up to whole tiles: the
+  // same iterations on the critical path, fewer splits to write and merge
+  // (the 65k-prefix request: 114 splits of 576 keys instead of 128 of 544).
+  auto whole_tiles = [](int64_t k) { return (k + TILE - 1) / TILE * TILE; };
+  int64_t keys_per_item = whole_tiles((units + cus - 1) / cus);
   if (keys_per_item < MIN_KEYS_PER_SPLIT) keys_per_item = MIN_KEYS_PER_SPLIT;
   int forced = 0;
   if (const char* e = std::getenv("VA_NSPLIT")) forced = std::atoi(e);
@@ -1112,7 +1117,7 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
         more |= ns > 1;
       }
       if (items <= cus || !more) break;
-      keys_per_item += std::max<int64_t>(SPLIT_ALIGN, keys_per_item / 64);
+      keys_per_item = whole_tiles(keys_per_item + std::max<int64_t>(SPLIT_ALIGN, keys_per_item / 64));
     }
   }
 

@@ -53,14 +53,16 @@ def test_plan_long_prefix_h8_t16():
     p = _plan(8, [65536], [16])
     assert p.magic == binding.VA_PLAN_MAGIC and p.rows_per_group == 64 and p.tile_keys == 64
     assert p.num_groups[0] == 2                     # 128 rows / 64
-    # keys x groups spread over 256 CUs: 2 * 65552 / 256 = 512 keys per work item
-    assert p.nsplit[0] == 128
-    assert p.total_work == 256
+    # keys x groups spread over 256 CUs: ceil(2 * 65552 / 256) = 513 keys per
+    # work item, i.e. 9 tile iterations; rounded up to whole tiles (576 keys)
+    # that is ceil(65552 / 576) = 114 splits
+    assert p.nsplit[0] == 114
+    assert p.total_work == 228
     assert p.total_tree == 16 and p.total_rows == 128
-    o = 256 * 64 * 512 * 2                          # fp16 partial outputs
+    o = 228 * 64 * 512 * 2                          # fp16 partial outputs
     assert p.lse_offset == o
-    assert p.status_offset == o + 256 * 64 * 8
-    assert p.workspace_bytes == o + 256 * 64 * 8 + 1024
+    assert p.status_offset == o + 228 * 64 * 8
+    assert p.workspace_bytes == o + 228 * 64 * 8 + 1024
 
 
 def test_plan_full_heads_and_ragged_batch():
@@ -213,11 +215,12 @@ def test_plan_split_tree_adds_one_tree_split_per_request():
     p = va.verify_attn_plan(8, [65536], [16], num_cus=256, split_tree=True)
     assert p.mode == binding.VA_MODE_SPLIT_TREE
     # prefix keys x groups over the 254 CUs the 2 tree-block items leave:
-    # ceil(2 * 65536 / 254) = 517 keys per prefix split -> 127 prefix splits
-    assert p.nsplit[0] == 127 + 1
-    assert p.total_work == 2 * 128
-    o = 2 * 128 * 64 * 512 * 2
-    assert p.workspace_bytes == o + 2 * 128 * 64 * 8 + 1024
+    # ceil(2 * 65536 / 254) = 517 keys per prefix split, rounded up to whole
+    # tiles (576) -> ceil(65536 / 576) = 114 prefix splits
+    assert p.nsplit[0] == 114 + 1
+    assert p.total_work == 2 * 115
+    o = 2 * 115 * 64 * 512 * 2
+    assert p.workspace_bytes == o + 2 * 115 * 64 * 8 + 1024
     q = va.verify_attn_plan(4, [0, 100, 5000], [3, 64, 9], num_cus=256, split_tree=True)
     assert all(ns >= 2 for ns in q.splits())                 # L = 0 keeps one (empty) prefix split
     assert q.work_begin[3] == sum(q.num_groups[r] * q.nsplit[r] for r in range(3))
