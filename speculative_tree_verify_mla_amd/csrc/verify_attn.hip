@@ -440,9 +440,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   // each) and the rope parts of the same keys (two copies of 8 rows).  Keys
   // past the split end and slots outside the pool copy the zero row.
   uint32_t bad = 0u;
-  // The copies of a tile are issued in ISSUE_PARTS pieces spread over the
-  // score MFMAs of the previous tile: a burst of all of them stalls the wave
-  // on memory back-pressure while the MFMA pipe idles.
+  // The copies of a tile are issued in 9 pieces of 2 spread over the score
+  // MFMAs of the previous tile: a burst of all of them stalls the wave on
+  // memory back-pressure while the MFMA pipe idles.
   struct TileIssue {
     int32_t vslot;   // slot of key `lane` of the tile
     uint64_t use;    // bit j: key j is read (exists and its slot is in the pool)
@@ -643,12 +643,13 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
 
   // ---- pipeline over the split's tiles (two buffers; tile u in buffer u % 2).
   // Per wave the copies are issued in the order
-  //   [slots 0, 1] (wait) [tile 0] [slots 2] | loop t: [slots t+3] [tile t+1]
-  // (slot copies on wave 0 only; the copies of tile t+1 are spread over the
-  // score MFMAs of tile t).  At the top of iteration t every wave waits for
-  // all its copies, which are those of tile t and the slots up to t+2.  The
-  // barrier then publishes tile t and slots t+1 and ends all use of tile
-  // t-1, whose buffer tile t+1 overwrites while tile t is consumed.
+  //   [slots 0, 1] [Q] (wait) [tile 0] [slots 2] | loop t: [slots t+3] [tile t+1]
+  // (slot copies on wave 0 only; Q goes to the second buffer in the first
+  // pass; the copies of tile t+1 are spread over the score MFMAs of tile t).
+  // At the top of iteration t every wave waits for all its copies, which are
+  // those of tile t and the slots up to t+2.  The barrier then publishes tile
+  // t and slots t+1 and ends all use of tile t-1 (or of the Q staging), whose
+  // buffer tile t+1 overwrites while tile t is consumed.
   uint64_t anc_row = 0ull;
   for (int pass = 0;; ++pass) {
 #pragma unroll
