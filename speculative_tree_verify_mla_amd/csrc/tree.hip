@@ -52,8 +52,16 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
   const bool live = lane < T;
   uint32_t bad = 0u;
 
-  // depth by walking up the chain; a walk longer than T means a cycle
+  // depth by walking up the chain: every lane holds its node's parent (one
+  // load), and the walk follows the chains through the wave.  A parent out
+  // of range flags the request and ends the chains through that node; a
+  // walk still going after 64 steps (more than T) is a cycle.
+  // every load up front: the walk, the ranking and the table write then need
+  // no further round trip to memory
   int p = live ? a.raw_parent[t0 + lane] : -1;
+  const int32_t my_slot = live ? a.raw_slot[t0 + lane] : 0;
+  const int64_t tab_lo = (int64_t)a.slot_indptr[r] + a.prefix_len[r];
+  const int32_t tab_hi = a.slot_indptr[r + 1];
   if (live && (p < -1 || p >= T)) {
     bad = VA_TREE_BAD_PARENT;
     p = -1;
@@ -61,19 +69,14 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
   int depth = 0;
   {
     int x = p;
-    while (live && x != -1 && bad == 0u) {
-      ++depth;
-      if (depth > T) {
-        bad = VA_TREE_BAD_PARENT;
-        break;
+    for (int step = 0; step < VA_MAX_TREE && __any(x >= 0); ++step) {   // uniform
+      const int nx = __shfl(p, x >= 0 ? x : 0);
+      if (x >= 0) {
+        ++depth;
+        x = nx;
       }
-      const int px = a.raw_parent[t0 + x];
-      if (px < -1 || px >= T) {
-        bad = VA_TREE_BAD_PARENT;
-        break;
-      }
-      x = px;
     }
+    if (x >= 0) bad = VA_TREE_BAD_PARENT;
   }
   // verify position = rank of (depth, raw index) among the live nodes
   const int key = live ? (depth << 6) | lane : 0x7fffffff;
@@ -82,11 +85,11 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
   const int prank = __shfl(rank, p < 0 ? 0 : p);
   // ancestor mask in verify positions: walk the chain again, mapping raw ids
   // to verify positions through the wave (every lane takes part in the
-  // shuffles; lanes with x = -1 idle)
+  // shuffles; lanes with x = -1 idle; the walk stops when every chain ended)
   uint64_t m = 0ull;
   {
     int x = (live && bad == 0u) ? lane : -1;
-    for (int step = 0; step < 64; ++step) {
+    for (int step = 0; step < VA_MAX_TREE && __any(x >= 0); ++step) {   // uniform
       const int rx = __shfl(rank, x < 0 ? 0 : x);
       const int nx = __shfl(p, x < 0 ? 0 : x);
       if (x >= 0) {
@@ -100,9 +103,9 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
     a.perm[o] = lane;
     a.parent[o] = p < 0 ? -1 : prank;
     a.anc[o] = m;
-    const int64_t e = (int64_t)a.slot_indptr[r] + a.prefix_len[r] + rank;
-    if (e >= 0 && e < a.slot_table_len && e < a.slot_indptr[r + 1])
-      a.slot_table[e] = a.raw_slot[t0 + lane];
+    const int64_t e = tab_lo + rank;
+    if (e >= 0 && e < a.slot_table_len && e < tab_hi)
+      a.slot_table[e] = my_slot;
     else
       bad |= VA_TREE_BAD_TABLE;
   }
