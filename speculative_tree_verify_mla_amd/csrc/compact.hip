@@ -156,6 +156,64 @@ __global__ __launch_bounds__(CB) void compact_select_kernel(CompactArgs a) {
   }
 }
 
+// The same selection without the scan launch, for tables of at most CB
+// count blocks: every block reduces the (at most CB) per-block counts itself
+// to its own offset, the total and the precondition bits; block 0 publishes
+// the result.
+__global__ __launch_bounds__(CB) void compact_select_fused_kernel(CompactArgs a) {
+  __shared__ int w_before[CB / 64];
+  __shared__ int w_total[CB / 64];
+  __shared__ uint32_t w_bits[CB / 64];
+  __shared__ int wcnt[CB / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  // this thread's count block (nblocks <= CB)
+  const int cnt = t < a.nblocks ? a.block_need[t] : 0;
+  const uint32_t cbad = t < a.nblocks ? a.block_bad[t] : 0u;
+  int before = t < (int)blockIdx.x ? cnt : 0;
+  int total = cnt;
+  uint32_t bits = cbad;
+  for (int o = 32; o >= 1; o >>= 1) {
+    before += __shfl_xor(before, o);
+    total += __shfl_xor(total, o);
+    bits |= __shfl_xor(bits, o);
+  }
+  if (lane == 0) {
+    w_before[wave] = before;
+    w_total[wave] = total;
+    w_bits[wave] = bits;
+  }
+  __syncthreads();
+  int off = 0, tot = 0;
+  uint32_t b = 0u;
+  for (int i = 0; i < CB / 64; ++i) {
+    off += w_before[i];
+    tot += w_total[i];
+    b |= w_bits[i];
+  }
+  const int todo = b ? -(int)b : (tot < a.budget ? tot : a.budget);
+  if (blockIdx.x == 0 && t == 0) {
+    a.result[0] = todo;
+    a.result[1] = (int)b;
+    *a.copied = todo;
+  }
+  if (todo <= 0) return;
+  const int k = blockIdx.x * CB + t;
+  bool need = false;
+  uint32_t bad = 0u;
+  if (k < a.n) classify(a, k, &need, &bad);
+  const uint64_t m = __ballot(need);
+  if (lane == 0) wcnt[wave] = __popcll(m);
+  __syncthreads();
+  for (int i = 0; i < wave; ++i) off += wcnt[i];
+  const int rank = off + __popcll(m & ((1ull << lane) - 1ull));
+  if (need && rank < todo) {
+    a.sel_pos[rank] = k;
+    a.sel_src[rank] = a.table[k];
+  }
+}
+
 // Copy piece p of selected row i (thread i * 72 + p), then rewrite the table
 // entry.  The copy reads only sel_src, never the table it rewrites.
 __global__ __launch_bounds__(COPY_THREADS) void compact_copy_kernel(CompactArgs a) {
@@ -241,8 +299,12 @@ int verify_attn_compact(uint16_t* kv_pool, int64_t num_slots, int32_t kv_row_str
   hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned nb = (unsigned)a.nblocks;
   hipLaunchKernelGGL(compact_count_kernel, dim3(nb), dim3(CB), 0, st, a);
-  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, st, a);
-  hipLaunchKernelGGL(compact_select_kernel, dim3(nb), dim3(CB), 0, st, a);
+  if (nb <= CB) {   // every block can reduce the counts itself: no scan launch
+    hipLaunchKernelGGL(compact_select_fused_kernel, dim3(nb), dim3(CB), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(compact_select_kernel, dim3(nb), dim3(CB), 0, st, a);
+  }
   const int64_t threads = (int64_t)budget * ROW_PIECES;
   const unsigned copy_blocks = (unsigned)((threads + COPY_THREADS - 1) / COPY_THREADS);
   if (copy_blocks > 0)

@@ -133,3 +133,16 @@ def test_compaction_in_a_graph_replays():
     assert int(copied.item()) == c2 == 500
     np.testing.assert_array_equal(tab.cpu().numpy(), t2)
     assert np.array_equal(_pool_u16(kv), p2)
+
+
+def test_table_over_a_million_entries_uses_the_scan_pass():
+    """More than 1024 count blocks (n > 2^20): the separate scan pass, with its
+    carry across chunks of 1024 counts, selects the rows.  Slots come from a
+    small range (duplicates are separate keys) so the pool stays ~1.2 GB."""
+    rng = np.random.default_rng(9)
+    n, src_slots = (1 << 20) + 1500, 4096
+    pool = np.zeros((src_slots + n, 576), np.uint16)
+    pool[:src_slots] = inputs.normal_bf16(rng, (src_slots, 576))
+    table = rng.integers(0, src_slots, size=n).astype(np.int32)
+    for budget in (5000, 0):
+        _check(table, pool, src_slots, budget, "n > 2^20")
