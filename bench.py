@@ -207,8 +207,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU verify path only; this build runs on one GPU "
-              "(use --gpus 1).", file=sys.stderr)
+        print("bench.py measures the verify path on one GPU only; multi-GPU runs are not "
+              "supported (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
