@@ -45,8 +45,9 @@
 //     2^64), which bf16 and the fp32 accumulators hold without loss of
 //     relative precision, and the accumulators are never rescaled.  If a
 //     later tile beats a row's reference by more than 2^64 (only adversarial
-//     inputs do), the work item restarts from its first tile with the
-//     reference raised to the largest max seen.
+//     inputs do), the work item sweeps its split once for each row's exact
+//     max (scores only) and then computes the split again against that max,
+//     so every input takes at most three passes.
 //   - The tree mask is one 64-bit ancestor mask per draft node, built in the
 //     prologue from parent[]; only tiles reaching past the prefix consult it.
 //   - Each work item writes its normalised output o / lb (lb = the sum of the
@@ -90,7 +91,6 @@ constexpr int LAT_DMA = TILE / 4;    // latent rows one wave copies per tile
 constexpr int ROPE_DMA = TILE / 32;  // rope blocks (8 keys each) one wave copies per tile
 constexpr int MIN_KEYS_PER_SPLIT = 128;
 constexpr float REF_SLACK = 64.f;  // log2 units: probabilities stay <= 2^64
-constexpr int MAX_PASSES = 8;      // restarts of a work item with a raised reference
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -510,8 +510,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
 
   // Consumes tile t (one buffer).  `first` is set on the first tile of a
   // pass: the two key-half waves then agree on each row's reference.
+  // In the sweep pass (`sweep`) only the scores and their max are taken.
   auto compute = [&](int t, const uint16_t* buf, uint64_t anc_row, bool first,
-                     const TileIssue& nxt) {
+                     const TileIssue& nxt, bool sweep) {
     const int kt = k0 + t * TILE;
     // keep every Q fragment in an accumulation register for the whole loop:
     // the score MFMAs read them there directly, where the allocator would
@@ -570,6 +571,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     }
     mx *= a.scale_log2;
     m_seen = fmaxf(m_seen, mx);
+    if (sweep) return;   // uniform
     if (first) {
       // reference = the row's max over the whole tile (both key halves)
       if (lh == 0) xm[rh][kh][lrow] = mx;
@@ -577,7 +579,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       const float r2 = fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]);
       if (m_ref == -INFINITY) m_ref = r2;
     } else if (mx > m_ref + REF_SLACK) {
-      restart_sh = 1u;   // all waves restart the pass with a raised reference
+      restart_sh = 1u;   // all waves stop the pass; the sweep for the exact max follows
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     // probabilities exp2(s * scale - m); register quads 2ks, 2ks+1 form the
@@ -650,8 +652,15 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   // those of tile t and the slots up to t+2.  The barrier then publishes tile
   // t and slots t+1 and ends all use of tile t-1 (or of the Q staging), whose
   // buffer tile t+1 overwrites while tile t is consumed.
+  //
+  // Passes: pass 0 computes the split against each row's first tile max.  If
+  // a later tile beats that reference by more than REF_SLACK, pass 0 stops
+  // and pass 1 sweeps every tile of the split for each row's exact max
+  // (scores only, nothing accumulated); pass 2 then computes the split
+  // against that max, which no tile can exceed, so no input needs a fourth.
   uint64_t anc_row = 0ull;
   for (int pass = 0;; ++pass) {
+    const bool sweep = pass == 1;
 #pragma unroll
     for (int c = 0; c < O_HALF; ++c) {
 #pragma unroll
@@ -694,7 +703,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     for (int t = 0; t < ntiles; ++t) {
       vm_wait<0>();
       lds_barrier();   // tile t is in LDS; every wave is done with tile t-1
-      if (restart_seen && pass + 1 < MAX_PASSES) {   // uniform
+      if (restart_seen && pass == 0) {   // uniform
         restart = true;
         break;
       }
@@ -703,12 +712,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       const TileIssue nxt = prepare_tile(t + 1, vslot_next, tiles + ((t + 1) & 1) * BUF_ELEMS);
       vslot_next = sring[(t + 2) & (SLOT_RING - 1)][lane];
       issue_slots(t + 3);
-      compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0, nxt);
-      value_half(tiles + (t & 1) * BUF_ELEMS, kh, pown);
+      compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0, nxt, sweep);
+      if (!sweep) value_half(tiles + (t & 1) * BUF_ELEMS, kh, pown);
       lds_barrier();   // both key halves' probabilities are in LDS
       // every write of restart_sh (in compute) precedes the barrier above
       const uint32_t rs = restart_sh;
-      {
+      if (!sweep) {
         bf16x8 poth[2];
         poth[0] = xp[rh][kh ^ 1][0][lane];
         poth[1] = xp[rh][kh ^ 1][1][lane];
@@ -718,9 +727,10 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     }
     vm_wait<0>();
     __syncthreads();   // all copies landed and all waves are done with the tiles
-    if (!restart) restart = restart_sh != 0u && pass + 1 < MAX_PASSES;
+    if (!restart) restart = sweep || (pass == 0 && restart_sh != 0u);
     if (!restart) break;
-    // raise the reference to the largest tile max either key half has seen
+    // the reference of the next pass: the largest tile max either key half
+    // has seen (after the sweep, the row's max over the whole split)
     if (lh == 0) xm[rh][kh][lrow] = m_seen;
     __syncthreads();
     m_ref = fmaxf(xm[rh][0][lrow], xm[rh][1][lrow]);

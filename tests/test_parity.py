@@ -248,6 +248,38 @@ def test_needle_on_draft_nodes_respects_the_tree():
         check(wl, out, lse, what=f"draft needle {j}")
 
 
+def _rising(L, T, step, seed):
+    """Prefix keys whose scores climb by about `step` log2 units from each
+    64-key tile to the next: every row of tile j gets j * c added to its 64
+    rope columns (q is 0.5 + 0.1 N(0, 1), so the score rises by about 32 c,
+    a little differently for every query row), while the value columns stay
+    N(0, 1)."""
+    H = 2
+    wl = inputs.make_workload("rising", H, [T], [L], 4 * (L + T) + 64, seed=seed)
+    rng = np.random.default_rng(seed)
+    wl.q = inputs.bf16_bits((0.5 + 0.1 * rng.standard_normal((T, H, 576))).astype(np.float32))
+    log2_per_unit = 0.5 * 64 * wl.sm_scale / math.log(2.0)   # score rise per unit of c
+    c = step / log2_per_unit
+    pool = inputs.bf16_to_f32(wl.kv_pool)
+    for k in range(L):
+        pool[wl.slot_table[k], 512:] += np.float32(c * (k // 64))
+    wl.kv_pool = inputs.bf16_bits(pool)
+    return wl
+
+
+@pytest.mark.parametrize("nsplit", [1, 3])
+def test_scores_rising_past_the_reference_on_every_tile(nsplit, monkeypatch):
+    """Tile maxima 100 log2 units apart over 12 tiles: each tile beats the
+    previous one by more than the fixed-reference slack (64), so a split
+    must find its exact max before its final pass.  The result is still the
+    plain softmax attention of the oracle, with finite values everywhere."""
+    monkeypatch.setenv("VA_NSPLIT", str(nsplit))
+    wl = _rising(L=64 * 12, T=4, step=100.0, seed=11)
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0
+    check(wl, out, lse, what=f"rising scores nsplit={plan.splits()}")
+
+
 # --------------------------------------------------------------------------- bit-exactness
 def test_permuted_pool_gives_identical_bits():
     wl = inputs.make_workload("perm", 8, [16], [5000], 16384, seed=13)

@@ -15,8 +15,8 @@ import torch
 import oracle
 import speculative_tree_verify_mla_amd as va
 from speculative_tree_verify_mla_amd import binding, inputs
-from test_parity import (DEV, EDGE, LSE_TOL, OUT_TOL, Dev, _needle, check, run_gpu, sample_rows,
-                         say)
+from test_parity import (DEV, EDGE, LSE_TOL, OUT_TOL, Dev, _needle, _rising, check, run_gpu,
+                         sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +114,16 @@ def test_split_needles_at_the_prefix_tree_seam():
             near = np.abs(got[i] - v).max() <= OUT_TOL
             assert near == (key < L or bool(vis[i, key - L])), (key, i)
         say(f"  split needle key={key} ok")
+
+
+def test_split_scores_rising_past_the_reference_on_every_tile(monkeypatch):
+    """The prefix kernel's splits see tile maxima 100 log2 units apart (more
+    than the fixed-reference slack): the result is still the oracle's."""
+    monkeypatch.setenv("VA_NSPLIT", "3")
+    wl = _rising(L=64 * 12, T=4, step=100.0, seed=12)
+    out, lse, status, plan = run_split(wl)
+    assert status == 0
+    check(wl, out, lse, what=f"split rising scores nsplit={plan.splits()}")
 
 
 def test_split_graph_capture_replays_bit_exact_and_follows_device_lengths():
