@@ -401,10 +401,19 @@ def main():
             t_cpu += time.time() - c0
             reps += 1
         per_call = t_cpu / reps
+        # one core: every 8th query row of the same call, scaled to all rows
+        sub = list(range(0, rows, 8))
+        c0 = time.time()
+        oracle.verify_attn_workload(wl, rows=sub, num_threads=1)
+        per_call_1 = (time.time() - c0) * rows / len(sub)
         cpu = {"value": round(kv_bytes / per_call / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{reps} full verify call(s) of the bench workload "
-                         f"({rows} rows x {n_keys} keys, fp64), {per_call * 1e3:.0f} ms/call"}
+                         f"({rows} rows x {n_keys} keys, fp64), {per_call * 1e3:.0f} ms/call",
+               "single_core": {"value": round(kv_bytes / per_call_1 / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "ms_per_call": round(per_call_1 * 1e3, 1),
+                               "sample": f"{len(sub)} of the {rows} rows (every 8th), "
+                                         f"time scaled by {rows / len(sub):g}"}}
         got = ref_out.float().cpu().numpy().astype(np.float64)
         parity = {"max_abs_out": float(np.abs(got - ref).max()),
                   "max_abs_lse": float(np.abs(lse.cpu().numpy() - ref_lse).max())}
