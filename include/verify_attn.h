@@ -186,7 +186,8 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
  * prefix_len     [B] int32 device: actual L_r, 0..planned bound.
  * parent         [sum T_r] int32, request-local: parent[i] in [-1, i-1]
  *                (-1: the node hangs directly off the prefix).
- * sm_scale       softmax scale applied to <q, k> (the workloads use 1/sqrt(192)).
+ * sm_scale       softmax scale applied to <q, k> (the workloads use 1/sqrt(192)); a
+ *                non-finite value is refused with VA_ERR_SHAPE.
  * workspace      device scratch of at least plan->workspace_bytes, 256-byte
  *                aligned; needs no initialisation.
  * stream         hipStream_t to enqueue on.

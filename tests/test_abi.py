@@ -128,11 +128,11 @@ def _fake(addr):
 
 
 def _run(lib, plan, q=4096, kv=8192, num_slots=100, stride=576, tab=64, ind=64, pl=64, par=64,
-         ws=1 << 20, ws_bytes=None):
+         ws=1 << 20, ws_bytes=None, sm_scale=0.1):
     ws_bytes = plan.workspace_bytes if ws_bytes is None else ws_bytes
     return lib.verify_attn_run(ctypes.byref(plan), _fake(q), _fake(kv), num_slots, stride,
-                               _fake(tab), 1000, _fake(ind), _fake(pl), _fake(par), 0.1, _fake(ws),
-                               ws_bytes, None)
+                               _fake(tab), 1000, _fake(ind), _fake(pl), _fake(par), sm_scale,
+                               _fake(ws), ws_bytes, None)
 
 
 def test_run_argument_errors_are_caught_before_launch():
@@ -145,6 +145,8 @@ def test_run_argument_errors_are_caught_before_launch():
     assert _run(lib, plan, stride=580) == -3              # stride not a multiple of 8
     assert _run(lib, plan, stride=512) == -2              # stride below 576
     assert _run(lib, plan, num_slots=0) == -2
+    assert _run(lib, plan, sm_scale=float("nan")) == -2
+    assert _run(lib, plan, sm_scale=float("inf")) == -2
     assert _run(lib, plan, ws=0) == -4
     assert _run(lib, plan, ws=(1 << 20) + 16) == -4       # not 256-byte aligned
     assert _run(lib, plan, ws_bytes=plan.workspace_bytes - 1) == -4
