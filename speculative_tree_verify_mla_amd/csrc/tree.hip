@@ -126,8 +126,11 @@ int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const
       slot_indptr == nullptr || slot_table == nullptr || perm == nullptr || parent == nullptr ||
       anc == nullptr || status == nullptr)
     return VA_ERR_NULL;
+  // the kernel indexes the caller's arrays through tree_begin: it must start
+  // at 0 and step by each request's tree size, as the planner writes it
   if (plan->magic != VA_PLAN_MAGIC || plan->version != VA_PLAN_VERSION ||
-      plan->num_requests < 1 || plan->num_requests > VA_MAX_REQUESTS)
+      plan->num_requests < 1 || plan->num_requests > VA_MAX_REQUESTS || plan->tree_begin[0] != 0 ||
+      plan->total_tree != plan->tree_begin[plan->num_requests])
     return VA_ERR_PLAN;
   for (int r = 0; r < plan->num_requests; ++r)
     if (plan->num_tree[r] < 1 || plan->num_tree[r] > VA_MAX_TREE ||

@@ -273,3 +273,26 @@ def test_plans_fit_the_compute_units(split_tree):
         prefix_items = sum(g * n for g, n in zip(groups, prefix_splits))
         assert prefix_items <= max(budget, 1) or all(n == 1 for n in prefix_splits), (H, L, T, cus, ns)
         assert p.total_work == sum(g * n for g, n in zip(groups, ns))
+
+
+@pytest.mark.parametrize("field,value", [("magic", 0), ("tree_begin0", 7), ("tree_size", 3),
+                                         ("total_tree", 99)])
+def test_build_tree_refuses_tampered_plans_before_launch(field, value):
+    """The marshaling kernel indexes the caller's arrays through the plan's
+    tree offsets; a plan whose offsets do not start at 0 and step by each
+    request's tree size is refused (no launch, so no GPU)."""
+    lib = va.load_library()
+    plan = _plan(8, [100, 50], [4, 6])
+    bad = binding.VaPlan()
+    ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
+    if field == "magic":
+        bad.magic = value
+    elif field == "tree_begin0":
+        bad.tree_begin[0] = value
+    elif field == "tree_size":
+        bad.tree_begin[1] = value   # request 0 would span 3 nodes, not 4
+    else:
+        bad.total_tree = value
+    f = _fake
+    assert lib.verify_attn_build_tree(ctypes.byref(bad), f(4096), f(4096), f(4096), f(4096),
+                                      f(4096), 100, f(4096), f(4096), f(4096), f(4096), None) == -5
