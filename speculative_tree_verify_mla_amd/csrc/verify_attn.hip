@@ -23,7 +23,9 @@
 //     own key half before that barrier and the other half's after it.
 //   - The group's Q rows are copied once into the second tile buffer in the
 //     tile layout, each wave reads its fragments from there, and the first
-//     tile's barrier frees the buffer for the second tile.
+//     tile's barrier frees the buffer for the second tile.  The first tile's
+//     copies go out as soon as its slot-table entries have landed, while Q
+//     is still in flight.
 //   - Tiles of 64 pool rows go straight from HBM into LDS with
 //     global_load_lds_dwordx4 (1 KB per wave instruction), double-buffered:
 //     one tile is in flight while the other is consumed.  The slot-table
@@ -49,7 +51,8 @@
 //     max (scores only) and then computes the split again against that max,
 //     so every input takes at most three passes.
 //   - The tree mask is one 64-bit ancestor mask per draft node, built in the
-//     prologue from parent[]; only tiles reaching past the prefix consult it.
+//     prologue from parent[] (copied into the slot ring's last row beside the
+//     first slot entries); only tiles reaching past the prefix consult it.
 //   - Each work item writes its normalised output o / lb (lb = the sum of the
 //     bf16 weights) in fp16 with a per-row power-of-two scale, in the MFMA
 //     output layout (512 B per wave store, streaming stores: only the merge
@@ -378,6 +381,11 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     issue_slots(0);
     issue_slots(1);
   }
+  // the parent entries of the request's draft nodes go to the slot ring's
+  // last row (free until the first tile is consumed); lanes past T re-read
+  // entry T-1
+  if (MODE != PREFIX && wave == 0)
+    dma4_v(lds_addr(&sring[SLOT_RING - 1][0]), a.parent + a.tree_begin[r] + min(lane, T - 1));
 
   // ---- Q, all 576 score columns of the group's rows
   const int rho = g * ROWS + rh * 32 + lrow;
@@ -410,29 +418,6 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       dma16_v_keep(qbuf + (LAT_ELEMS + kb * DROPE) * 2,
                    q0 + (int64_t)rr * DQK + DV + rope_piece(i, lane & 7) * 8);
     }
-  }
-
-  // ---- ancestor masks (bit j of anc[i]: draft node j is i or an ancestor of
-  // i).  Lane i of wave 0 holds node i's parent; the chains are followed
-  // through the wave, so the parent array is read once.
-  if (MODE != PREFIX && wave == 0) {
-    const int32_t* par = a.parent + a.tree_begin[r];
-    int p = lane < T ? par[lane] : -1;
-    if (p < -1 || p >= lane) {   // parents precede their children
-      st |= VA_STATUS_BAD_PARENT;
-      p = -1;
-    }
-    uint64_t m = lane < T ? 1ull << lane : 0ull;
-    // every step moves to a smaller index, so the walk ends within T steps
-    int x = p;
-    while (__any(x >= 0)) {
-      const int nx = __shfl(p, x >= 0 ? x : 0);
-      if (x >= 0) {
-        m |= 1ull << x;
-        x = nx;
-      }
-    }
-    anc[lane] = m;
   }
 
   // ---- tile loader.  For tile u, lane l takes the slot of key l from the
@@ -645,9 +630,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
 
   // ---- pipeline over the split's tiles (two buffers; tile u in buffer u % 2).
   // Per wave the copies are issued in the order
-  //   [slots 0, 1] [Q] (wait) [tile 0] [slots 2] | loop t: [slots t+3] [tile t+1]
-  // (slot copies on wave 0 only; Q goes to the second buffer in the first
-  // pass; the copies of tile t+1 are spread over the score MFMAs of tile t).
+  //   [slots 0, 1] [parents] [Q] (wait for all but Q) [tile 0] [slots 2]
+  //   (wait for Q) | loop t: [slots t+3] [tile t+1]
+  // (slot and parent copies on wave 0 only; Q goes to the second buffer in
+  // the first pass; the copies of tile t+1 are spread over the score MFMAs of
+  // tile t).  The waits before the loop rely on a wave's copies completing
+  // in the order they were issued.
   // At the top of iteration t every wave waits for all its copies, which are
   // those of tile t and the slots up to t+2.  The barrier then publishes tile
   // t and slots t+1 and ends all use of tile t-1 (or of the Q staging), whose
@@ -669,16 +657,53 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     l_run = 0.f;
     lb_run = 0.f;
     if (tid == 0) restart_sh = 0u;
-    if (ntiles > 0 && pass > 0) {   // the first pass's went out at the start
-      issue_slots(0);
-      issue_slots(1);
+    if (pass > 0) {
+      if (ntiles > 0) {
+        issue_slots(0);
+        issue_slots(1);
+      }
+      wait_vmcnt<0>();
+      __syncthreads();   // slots 0, 1 and restart_sh ready
+    } else {
+      // wave 0's slot and parent entries went out before its 18 Q copies
+      vm_wait<LAT_DMA + ROPE_DMA>();
+      __syncthreads();   // slots 0, 1, parents, status_sh and restart_sh ready
     }
-    // compiler-visible wait: also completes the Q loads, so the compiler adds
-    // no wait of its own before their first use
-    wait_vmcnt<0>();
-    __syncthreads();   // slots 0, 1, Q, anc[], status_sh and restart_sh ready
-    if (pass == 0 && MODE != PREFIX) anc_row = row_ok ? anc[rho / H] : 0ull;
+    if (ntiles > 0) {
+      // tile 0 goes out without waiting for Q, which fills the other buffer
+      const TileIssue first_tile = prepare_tile(0, sring[0][lane], tiles);
+#pragma unroll
+      for (int g = 0; g < 9; ++g) issue_part(first_tile, g);
+      issue_slots(2);
+    }
     if (pass == 0) {
+      if (MODE != PREFIX && wave == 0) {
+        int p = lane < T ? sring[SLOT_RING - 1][lane] : -1;
+        if (p < -1 || p >= lane) {   // parents precede their children
+          st |= VA_STATUS_BAD_PARENT;
+          p = -1;
+        }
+        uint64_t m = lane < T ? 1ull << lane : 0ull;
+        // every step moves to a smaller index, so the walk ends within T steps
+        int x = p;
+        while (__any(x >= 0)) {
+          const int nx = __shfl(p, x >= 0 ? x : 0);
+          if (x >= 0) {
+            m |= 1ull << x;
+            x = nx;
+          }
+        }
+        anc[lane] = m;
+      }
+      // this wave's Q copies precede its tile-0 copies (and wave 0's slot copy)
+      if (ntiles > 0) {
+        if (wave == 0) vm_wait<LAT_DMA + ROPE_DMA + 1>();
+        else vm_wait<LAT_DMA + ROPE_DMA>();
+      } else {
+        vm_wait<0>();
+      }
+      __syncthreads();   // Q and anc[] ready
+      if (MODE != PREFIX) anc_row = row_ok ? anc[rho / H] : 0ull;
       const uint16_t* const qb = tiles + BUF_ELEMS;
       const int qr = rh * HALF + lrow;
 #pragma unroll
@@ -687,12 +712,6 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
                                       : LAT_ELEMS + qr * DROPE + rope_piece(qr, 2 * (k - LAT_STEPS) + lh) * 8;
         qf[k] = *reinterpret_cast<const bf16x8*>(qb + off);
       }
-    }
-    if (ntiles > 0) {
-      const TileIssue first_tile = prepare_tile(0, sring[0][lane], tiles);
-#pragma unroll
-      for (int g = 0; g < 9; ++g) issue_part(first_tile, g);
-      issue_slots(2);
     }
 
     bool restart = false;
