@@ -280,6 +280,41 @@ def test_scores_rising_past_the_reference_on_every_tile(nsplit, monkeypatch):
     check(wl, out, lse, what=f"rising scores nsplit={plan.splits()}")
 
 
+# --------------------------------------------------------------------------- maximum sizes
+def test_maximum_request_count():
+    """VA_MAX_REQUESTS (64) requests of mixed tree sizes and prefixes in one
+    call: every request's rows against the oracle."""
+    rng = np.random.default_rng(64)
+    B = binding.VA_MAX_REQUESTS
+    T = rng.integers(1, 65, size=B).tolist()
+    L = rng.integers(0, 1500, size=B).tolist()
+    wl = inputs.make_workload("max_b", 2, T, L, 2 * (sum(T) + sum(L)) + 64, seed=64,
+                              table="interleaved")
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0
+    check(wl, out, lse, what=f"B={B} work={plan.total_work}")
+
+
+def test_maximum_head_count_and_tree():
+    """1024 heads x 64 draft nodes = 65536 query rows (1024 row groups);
+    sampled rows of every group against the oracle."""
+    wl = inputs.make_workload("max_h", 1024, [64], [100], 4096, seed=65)
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0
+    check(wl, out, lse, rows=sample_rows(wl, per_group=1), what=f"H=1024 T=64 work={plan.total_work}")
+
+
+def test_maximum_split_count(monkeypatch):
+    """VA_MAX_SPLITS (256) splits of one request: the reduce's largest
+    instantiation merges them."""
+    monkeypatch.setenv("VA_NSPLIT", str(binding.VA_MAX_SPLITS))
+    wl = inputs.make_workload("max_s", 8, [16], [12000], 32768, seed=66)
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0
+    assert plan.splits() == [binding.VA_MAX_SPLITS]
+    check(wl, out, lse, what=f"nsplit={plan.splits()}")
+
+
 # --------------------------------------------------------------------------- bit-exactness
 def test_permuted_pool_gives_identical_bits():
     wl = inputs.make_workload("perm", 8, [16], [5000], 16384, seed=13)
