@@ -41,6 +41,30 @@ WORKLOAD = 3                   # 1 request, H=8, T=16, L=65536
 N_POOLS = 8
 
 
+# The partial pass counts as held back by HBM only when the same launches
+# with the pool resident in the 256 MB Infinity Cache (warm) run clearly
+# faster than with the pool rotated out of it (cold).
+HBM_LIMITED_WARM_RATIO = 0.9
+
+
+def roofline_bound(flops, nbytes):
+    """Which roofline bounds a kernel of this arithmetic intensity: below
+    the ridge (peak flops / peak bytes per second) the HBM one."""
+    ridge = BF16_DENSE_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "hbm" if flops / nbytes < ridge else "mfma"
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 KERNEL_SRC = os.path.join(ROOT, "speculative_tree_verify_mla_amd", "csrc", "verify_attn.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_va_partial_kernel_tp_rank_h8_t16_l65536.txt")
 
@@ -183,6 +207,66 @@ def measure_marshal(torch, va, inputs, dev, time_graph):
     return res
 
 
+def measure_config(torch, va, inputs, dev, stream, idx, n_pools, steps):
+    """One of the other workloads (full head count, ragged batch): µs per call
+    from a HIP graph of `steps` calls rotating over `n_pools` pool copies,
+    effective KV GB/s and MFMA use against the dense bf16 peak."""
+    t0 = time.time()
+    wl = inputs.make_config(idx)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q = to_dev(wl.q.view(np.int16)).view(torch.bfloat16)
+    pool0 = to_dev(wl.kv_pool.view(np.int16)).view(torch.bfloat16)
+    pools = [pool0] + [pool0.clone() for _ in range(n_pools - 1)]
+    table, indptr = to_dev(wl.slot_table), to_dev(wl.slot_indptr)
+    prefix, parent = to_dev(wl.prefix_len), to_dev(wl.parent)
+    H = wl.num_heads
+    T = int(wl.num_tree.sum())
+    plan = va.verify_attn_plan(H, wl.prefix_len, wl.num_tree)
+    ws = va.workspace_for(plan, dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def step(i, reduce=True):
+        va.verify_attn_run(plan, q, pools[i % n_pools], table, indptr, prefix, parent,
+                           wl.sm_scale, ws, stream)
+        if reduce:
+            va.verify_attn_reduce(plan, ws, out, lse, stream)
+
+    with torch.cuda.stream(stream):
+        step(0)
+    torch.cuda.synchronize()
+    if va.verify_attn_read_status(plan, ws, stream) != 0:
+        raise RuntimeError(f"config {idx}: device status")
+    time_graph = capture_timer(torch, stream)
+    ms = time_graph(step, steps)
+    ms_partial = time_graph(lambda i: step(i, reduce=False), steps)
+    n_row_keys = sum(int(T_r) * H * (int(L_r) + int(T_r))
+                     for T_r, L_r in zip(wl.num_tree, wl.prefix_len))
+    flops = 2.0 * n_row_keys * (576 + 512)
+    kv_bytes = wl.kv_bytes()
+    print(f"# config {idx} {wl.name}: {ms * 1e3:.1f} us/call ({time.time() - t0:.1f}s)",
+          file=sys.stderr, flush=True)
+    return {
+        "workload": wl.name, "requests": len(wl.num_tree), "num_heads": H,
+        "num_tree": [int(x) for x in wl.num_tree], "prefix_len": [int(x) for x in wl.prefix_len],
+        "us_per_call": round(ms * 1e3, 3),
+        "partial_us": round(ms_partial * 1e3, 3),
+        "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "pct_hbm_peak": round(100.0 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+        "mfma_util_pct": round(100.0 * flops / (ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 2),
+        "partial_mfma_util_pct": round(100.0 * flops / (ms_partial * 1e-3) / 1e12
+                                       / BF16_DENSE_PEAK_TFLOPS, 2),
+        "nsplit": plan.splits(),
+        "work_items": int(plan.total_work),
+        "pools_rotated": n_pools,
+        "steps": steps,
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +285,8 @@ def parse():
                     help="skip the 2 GiB streaming-read calibration")
     ap.add_argument("--no-defrag", action="store_true",
                     help="skip the compaction (Tier 1 defrag) measurement")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the full-head and ragged-batch workloads")
     return ap.parse_args()
 
 
@@ -317,6 +403,7 @@ def main():
     ms_warm = timed(K, pool_set=[pools[0]])[0] / K
     ms_partial_warm = timed(K, reduce=False, pool_set=[pools[0]])[0] / K
     ms_split = timed(K, split=True)[0] / K
+    out_split = out.clone()        # the split-verify graph's output (all pool copies are equal)
     # spread: the same cold step graph (50 steps) replayed 11 times
     spread_n = 50
     with torch.cuda.stream(stream):
@@ -337,10 +424,8 @@ def main():
               "us_per_call_p10": round(float(np.percentile(per_call, 10)), 3),
               "us_per_call_p50": round(float(np.percentile(per_call, 50)), 3),
               "us_per_call_p90": round(float(np.percentile(per_call, 90)), 3)}
-    out_split = out.clone()
-    step(0)
-    torch.cuda.synchronize()
-    split_vs_fused = float((out_split.float() - out.float()).abs().max())
+    split_vs_fused = float((out_split.float() - ref_out.float()).abs().max())
+    split_bitwise_equal = bool(torch.equal(out_split.view(torch.int16), ref_out.view(torch.int16)))
     print(f"# timed {K} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
     kv_bytes = wl.kv_bytes()
@@ -365,6 +450,13 @@ def main():
                                 K, stream, capture_timer(torch, stream))
 
     marshal = measure_marshal(torch, va, inputs, dev, capture_timer(torch, stream))
+
+    other = None
+    if not args.no_other_configs:
+        # the MFMA-bound workloads: all 64 heads over a 200k prefix, and the
+        # ragged four-request batch (parity cases in the tests; timed here)
+        other = {"full_heads": measure_config(torch, va, inputs, dev, stream, 4, 3, 20),
+                 "ragged": measure_config(torch, va, inputs, dev, stream, 5, 2, 20)}
 
     stream_peak = None
     if not args.no_stream_peak:
@@ -407,7 +499,7 @@ def main():
         oracle.verify_attn_workload(wl, rows=sub, num_threads=1)
         per_call_1 = (time.time() - c0) * rows / len(sub)
         cpu = {"value": round(kv_bytes / per_call / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(), "nproc": os.cpu_count(),
                "sample": f"{reps} full verify call(s) of the bench workload "
                          f"({rows} rows x {n_keys} keys, fp64), {per_call * 1e3:.0f} ms/call",
                "single_core": {"value": round(kv_bytes / per_call_1 / 1e9, 4), "unit": "GB/s",
@@ -453,7 +545,11 @@ def main():
         "kv_bytes_per_call": kv_bytes,
         "roofline": {
             "kernel": "va_partial_kernel",
-            "bound": "hbm",
+            "bound": roofline_bound(flops, kv_bytes),
+            "arith_intensity_flop_per_byte": round(flops / kv_bytes, 1),
+            "ridge_flop_per_byte": round(BF16_DENSE_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS, 1),
+            "warm_over_cold": round(ms_partial_warm / ms_partial, 3),
+            "hbm_limited": bool(ms_partial_warm < HBM_LIMITED_WARM_RATIO * ms_partial),
             "achieved": round(gbs_partial, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -468,7 +564,9 @@ def main():
             "value": round(kv_bytes / (ms_split * 1e-3) / 1e9, 2),
             "nsplit": plan_split.splits(),
             "max_abs_out_vs_fused": split_vs_fused,
+            "bitwise_equal_to_fused": split_bitwise_equal,
         },
+        "other_configs": other,
         "defrag": defrag,
         "tree_marshal": marshal,
         "cpu_baseline": cpu,

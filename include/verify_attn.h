@@ -186,8 +186,10 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
  * prefix_len     [B] int32 device: actual L_r, 0..planned bound.
  * parent         [sum T_r] int32, request-local: parent[i] in [-1, i-1]
  *                (-1: the node hangs directly off the prefix).
- * sm_scale       softmax scale applied to <q, k> (the workloads use 1/sqrt(192)); a
- *                non-finite value is refused with VA_ERR_SHAPE.
+ * sm_scale       softmax scale applied to <q, k> (the workloads use 1/sqrt(192));
+ *                it must be finite and > 0 (the kernel takes the row max of the
+ *                unscaled scores and masks with -inf before scaling), anything
+ *                else is refused with VA_ERR_SHAPE.
  * workspace      device scratch of at least plan->workspace_bytes, 256-byte
  *                aligned; needs no initialisation.
  * stream         hipStream_t to enqueue on.
@@ -327,9 +329,11 @@ int verify_attn_compact(uint16_t* kv_pool, int64_t num_slots, int32_t kv_row_str
  * anc            [sum T_r] uint64 out: bit k set iff position k is i or an
  *                ancestor of i (the tree mask, as the kernel uses it).
  * status         [B] uint32 out: 0, or VA_TREE_* bits for a request whose
- *                raw tree is not a forest or whose table range is too short
- *                (then its outputs are unspecified; other requests are not
- *                affected).
+ *                raw tree is not a forest or whose draft entries do not all
+ *                fall inside its table range (a short range or a negative
+ *                device prefix length; entries outside the range are not
+ *                written, and its outputs are unspecified; other requests
+ *                are not affected).
  * One 64-lane wave per request; stream-ordered, graph-capture safe.
  * Errors (host): VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_SHAPE, VA_ERR_HIP.
  */

@@ -62,7 +62,8 @@ def marshal(num_tree, raw_parent, raw_slot, prefix_len, slot_indptr, slot_table)
         perm, parent, anc, bits = marshal_one(rp)
         for i in range(T):
             e = int(slot_indptr[r]) + int(prefix_len[r]) + i
-            if 0 <= e < min(len(table), int(slot_indptr[r + 1])):
+            # only inside the request's own range [slot_indptr[r], slot_indptr[r+1])
+            if max(0, int(slot_indptr[r])) <= e < min(len(table), int(slot_indptr[r + 1])):
                 table[e] = raw_slot[t0 + perm[i]]
             else:
                 bits |= BAD_TABLE

@@ -60,7 +60,8 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
   // no further round trip to memory
   int p = live ? a.raw_parent[t0 + lane] : -1;
   const int32_t my_slot = live ? a.raw_slot[t0 + lane] : 0;
-  const int64_t tab_lo = (int64_t)a.slot_indptr[r] + a.prefix_len[r];
+  const int32_t tab_base = a.slot_indptr[r];
+  const int64_t tab_lo = (int64_t)tab_base + a.prefix_len[r];
   const int32_t tab_hi = a.slot_indptr[r + 1];
   if (live && (p < -1 || p >= T)) {
     bad = VA_TREE_BAD_PARENT;
@@ -104,7 +105,9 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
     a.parent[o] = p < 0 ? -1 : prank;
     a.anc[o] = m;
     const int64_t e = tab_lo + rank;
-    if (e >= 0 && e < a.slot_table_len && e < tab_hi)
+    // only inside the request's own range [slot_indptr[r], slot_indptr[r+1]):
+    // a negative device prefix length must not reach the previous request
+    if (e >= 0 && e >= tab_base && e < a.slot_table_len && e < tab_hi)
       a.slot_table[e] = my_slot;
     else
       bad |= VA_TREE_BAD_TABLE;

@@ -1193,7 +1193,7 @@ int verify_attn_run(const va_plan* plan, const uint16_t* q, const uint16_t* kv_p
     return VA_ERR_NULL;
   if (!plan_ok(plan)) return VA_ERR_PLAN;
   if (num_slots < 1 || num_slots > (int64_t)INT32_MAX + 1 || kv_row_stride < DQK ||
-      slot_table_len < 0 || !std::isfinite(sm_scale))
+      slot_table_len < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return VA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(kv_pool) || (kv_row_stride % 8) != 0) return VA_ERR_ALIGN;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||

@@ -147,6 +147,8 @@ def test_run_argument_errors_are_caught_before_launch():
     assert _run(lib, plan, num_slots=0) == -2
     assert _run(lib, plan, sm_scale=float("nan")) == -2
     assert _run(lib, plan, sm_scale=float("inf")) == -2
+    assert _run(lib, plan, sm_scale=0.0) == -2             # masking needs a positive scale
+    assert _run(lib, plan, sm_scale=-0.1) == -2
     assert _run(lib, plan, ws=0) == -4
     assert _run(lib, plan, ws=(1 << 20) + 16) == -4       # not 256-byte aligned
     assert _run(lib, plan, ws_bytes=plan.workspace_bytes - 1) == -4

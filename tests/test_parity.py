@@ -70,71 +70,53 @@ def bf16_representation_error(ref):
     return np.abs(rb - ref)
 
 
-def check(wl, out, lse, rows=None, what="", raw=False):
-    """Compare with the oracle.  The output bound is 1e-2 beyond the bf16
-    representation error of the exact value (which alone reaches 7.8e-3 at
-    2 <= |o| < 4 and 1.6e-2 at 4 <= |o| < 8); with raw=True the plain
-    max |out - oracle| <= 1e-2 is required as well."""
+# From |x| = 4 up, neighbouring bf16 values are 2^-5 apart, so half that
+# spacing (1.6e-2) already exceeds OUT_TOL: there an output can only be held
+# to OUT_TOL beyond the rounding it must carry.  Below 4 the half spacing is
+# at most 7.8e-3 and the plain bound applies.
+REPR_FROM = 4.0
+
+
+def check(wl, out, lse, rows=None, what=""):
+    """Compare with the oracle, element by element.
+    Output: |out - oracle| <= 1e-2 wherever |oracle| < 4; where |oracle| >= 4,
+    |out - oracle| - (bf16 representation error of the oracle value) <= 1e-2.
+    LSE: |lse - oracle| <= 1e-3 on every row."""
     ref, ref_lse = oracle.verify_attn_workload(wl, rows=rows)
     got = out.float().cpu().numpy().reshape(-1, 512).astype(np.float64)
     gl = lse.cpu().numpy().reshape(-1)
     ref = ref.reshape(-1, 512)
     ref_lse = ref_lse.reshape(-1)
     sel = np.arange(got.shape[0]) if rows is None else np.asarray(sorted(rows))
-    diff = np.abs(got[sel] - ref[sel])
-    e = diff.max()
-    beyond = (diff - bf16_representation_error(ref[sel])).max()
+    r = ref[sel]
+    diff = np.abs(got[sel] - r)
+    small = np.abs(r) < REPR_FROM
+    e_small = diff[small].max() if small.any() else 0.0
+    beyond = diff - bf16_representation_error(r)
+    e_large = beyond[~small].max() if (~small).any() else 0.0
     el = np.abs(gl[sel] - ref_lse[sel]).max()
-    say(f"  {what} rows={len(sel)} max|out-oracle|={e:.3e} (beyond bf16 rounding {beyond:.3e}) "
-        f"max|lse-oracle|={el:.3e} max|oracle|={np.abs(ref[sel]).max():.2f}")
+    say(f"  {what} rows={len(sel)} max|out-oracle|={diff.max():.3e} (|oracle|<4: {e_small:.3e}; "
+        f"beyond bf16 rounding at |oracle|>=4: {e_large:.3e}, {int((~small).sum())} elements) "
+        f"max|lse-oracle|={el:.3e} max|oracle|={np.abs(r).max():.2f}")
     assert np.isfinite(got[sel]).all() and np.isfinite(gl[sel]).all()
-    assert beyond <= OUT_TOL, beyond
-    if raw:
-        assert e <= OUT_TOL, e
+    assert e_small <= OUT_TOL, e_small
+    assert e_large <= OUT_TOL, e_large
     assert el <= LSE_TOL, el
-    return e, el
-
-
-def sample_rows(wl, per_group=2, seed=0):
-    """A spread of rows: both ends of every 64-row group, plus random ones."""
-    rng = np.random.default_rng(seed)
-    rows = set()
-    base = 0
-    H = wl.num_heads
-    for T in wl.num_tree:
-        n = int(T) * H
-        for g0 in range(0, n, 64):
-            g1 = min(n, g0 + 64)
-            rows.update([base + g0, base + g1 - 1])
-            rows.update((base + rng.integers(g0, g1, size=per_group)).tolist())
-        base += n
-    return sorted(rows)
+    return diff.max(), el
 
 
 # --------------------------------------------------------------------------- the five workloads
-@pytest.mark.parametrize("idx", [1, 2, 3])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_config_parity_all_rows(idx):
+    """The five workloads, every output row against the oracle (the full-head
+    and ragged ones take the oracle about 12 s and 6 s on 16 host cores)."""
     wl = inputs.make_config(idx)
     say(f"config {idx} {wl.name}: H={wl.num_heads} T={wl.num_tree.tolist()} "
         f"L={wl.prefix_len.tolist()}")
     out, lse, status, plan = run_gpu(wl)
     assert status == 0
     say(f"  nsplit={plan.splits()} work={plan.total_work}")
-    check(wl, out, lse, what=f"config {idx}", raw=True)
-
-
-@pytest.mark.parametrize("idx", [4, 5])
-def test_config_parity_sampled_rows(idx):
-    wl = inputs.make_config(idx)
-    say(f"config {idx} {wl.name}: H={wl.num_heads} T={wl.num_tree.tolist()} "
-        f"L={wl.prefix_len.tolist()}")
-    out, lse, status, plan = run_gpu(wl)
-    assert status == 0
-    say(f"  nsplit={plan.splits()} work={plan.total_work}")
-    check(wl, out, lse, rows=sample_rows(wl), what=f"config {idx}", raw=True)
-    # every row: finite, and lse at least the log of the prefix length
-    o = out.float()
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    check(wl, out, lse, what=f"config {idx}")
 
 
 # --------------------------------------------------------------------------- shapes and edges
@@ -296,12 +278,12 @@ def test_maximum_request_count():
 
 
 def test_maximum_head_count_and_tree():
-    """1024 heads x 64 draft nodes = 65536 query rows (1024 row groups);
-    sampled rows of every group against the oracle."""
+    """1024 heads x 64 draft nodes = 65536 query rows, every row against the
+    oracle."""
     wl = inputs.make_workload("max_h", 1024, [64], [100], 4096, seed=65)
     out, lse, status, plan = run_gpu(wl)
     assert status == 0
-    check(wl, out, lse, rows=sample_rows(wl, per_group=1), what=f"H=1024 T=64 work={plan.total_work}")
+    check(wl, out, lse, what=f"H=1024 T=64 work={plan.total_work}")
 
 
 def test_maximum_split_count(monkeypatch):

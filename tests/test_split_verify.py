@@ -16,7 +16,7 @@ import oracle
 import speculative_tree_verify_mla_amd as va
 from speculative_tree_verify_mla_amd import binding, inputs
 from test_parity import (DEV, EDGE, LSE_TOL, OUT_TOL, Dev, _needle, _rising, check, run_gpu,
-                         sample_rows, say)
+                         say)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,24 +32,14 @@ def run_split(wl, d=None, prefix_host=None):
     return run_gpu(wl, d=d, plan=plan)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_split_config_parity_all_rows(idx):
     wl = inputs.make_config(idx)
     say(f"split config {idx} {wl.name}")
     out, lse, status, plan = run_split(wl)
     assert status == 0
     say(f"  nsplit={plan.splits()} (prefix splits + tree block) work={plan.total_work}")
-    check(wl, out, lse, what=f"split config {idx}", raw=True)
-
-
-@pytest.mark.parametrize("idx", [4, 5])
-def test_split_config_parity_sampled_rows(idx):
-    wl = inputs.make_config(idx)
-    say(f"split config {idx} {wl.name}")
-    out, lse, status, plan = run_split(wl)
-    assert status == 0
-    check(wl, out, lse, rows=sample_rows(wl), what=f"split config {idx}", raw=True)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    check(wl, out, lse, what=f"split config {idx}")
 
 
 @pytest.mark.parametrize("case", EDGE, ids=lambda c: f"H{c[0]}_T{c[1]}_L{c[2]}_{c[3]}")

@@ -97,6 +97,25 @@ def test_bad_trees_are_flagged_per_request():
     assert got2[3][2] & ot.BAD_TABLE
 
 
+def test_negative_device_prefix_writes_only_its_own_table_range():
+    """A negative prefix length puts some of a request's draft entries below
+    its table range: they are not written (the previous request's entries
+    stay as they were) and the request is flagged."""
+    wl, rp, rs, _ = _raw_batch([6, 8, 5], [20, 30, 40], seed=13)
+    prefix = wl.prefix_len.copy()
+    prefix[1] = -3
+    wl2 = inputs.Workload(**{**wl.__dict__, "prefix_len": prefix})
+    before = wl.slot_table.copy()
+    ref = ot.marshal(wl2.num_tree, rp, rs, prefix, wl.slot_indptr, before)
+    got = _gpu_marshal(wl2, rp, rs, before)
+    assert got[3][1] & ot.BAD_TABLE and got[3][0] == 0 and got[3][2] == 0
+    np.testing.assert_array_equal(got[4], ref[4])
+    # request 0's range holds exactly what a run with a valid request 1 writes
+    ok = ot.marshal(wl.num_tree, rp, rs, wl.prefix_len, wl.slot_indptr, before)
+    e0, e1 = int(wl.slot_indptr[0]), int(wl.slot_indptr[1])
+    np.testing.assert_array_equal(got[4][e0:e1], ok[4][e0:e1])
+
+
 def test_marshal_then_verify_in_one_graph():
     """Raw trees in, verify outputs out, all captured in one HIP graph; rows
     come out in verify order and match the oracle on the marshaled inputs."""
@@ -138,4 +157,4 @@ def test_marshal_then_verify_in_one_graph():
     perm_h = ref[0]
     q_v = np.concatenate([q_raw[:16][perm_h[:16]], q_raw[16:][perm_h[16:]]])
     wl_v = inputs.Workload(**{**wl.__dict__, "q": q_v, "parent": ref[1], "slot_table": ref[4]})
-    check(wl_v, out, lse, what="marshal+verify graph", raw=True)
+    check(wl_v, out, lse, what="marshal+verify graph")

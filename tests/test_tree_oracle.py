@@ -84,3 +84,25 @@ def test_marshaled_tree_attends_like_the_raw_tree(seed):
             assert abs(lse[i, h] - l) <= 1e-12
         m = int(anc[i])
         assert bin(m).count("1") == len(chain)
+
+
+def test_draft_entries_stay_inside_the_request_range():
+    """Each request's draft entries go to slot_indptr[r] + prefix_len[r] + i
+    only while that index lies in [slot_indptr[r], slot_indptr[r+1]): a
+    negative prefix length of request 1 flags it and leaves request 0's
+    range exactly as a valid batch leaves it."""
+    num_tree = [3, 4]
+    raw_parent = np.array([-1, 0, 0, -1, 0, 1, 1], np.int32)
+    raw_slot = np.arange(7, dtype=np.int32) + 500
+    indptr = [0, 10, 20]
+    table = np.arange(20, dtype=np.int32)
+    ok = ot.marshal(num_tree, raw_parent, raw_slot, [7, 6], indptr, table)
+    bad = ot.marshal(num_tree, raw_parent, raw_slot, [7, -2], indptr, table)
+    assert ok[3].tolist() == [0, 0]
+    assert bad[3][0] == 0 and bad[3][1] & ot.BAD_TABLE
+    # request 0: prefix 0..6 untouched, its drafts at 7..9 in breadth-first order
+    assert bad[4][:10].tolist() == list(range(7)) + [500, 501, 502]
+    np.testing.assert_array_equal(bad[4][:10], ok[4][:10])
+    # request 1: entry 10 + (-2) + i is inside its range for i >= 2 only
+    assert bad[4][10:12].tolist() == [505, 506]
+    assert bad[4][12:].tolist() == list(range(12, 20))
