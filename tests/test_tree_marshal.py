@@ -36,11 +36,12 @@ def _raw_batch(num_tree, prefix, seed, slots=4096):
     return wl, raw_parent, raw_slot, q_raw
 
 
-def _gpu_marshal(wl, raw_parent, raw_slot, table):
+def _gpu_marshal(wl, raw_parent, raw_slot, table, device_prefix=None):
     plan = va.verify_attn_plan(wl.num_heads, wl.prefix_len, wl.num_tree)
     tab = _t(table)
+    pre = wl.prefix_len if device_prefix is None else np.asarray(device_prefix, np.int32)
     perm, parent, anc, status = va.verify_attn_build_tree(
-        plan, _t(raw_parent), _t(raw_slot), _t(wl.prefix_len), _t(wl.slot_indptr), tab)
+        plan, _t(raw_parent), _t(raw_slot), _t(pre), _t(wl.slot_indptr), tab)
     torch.cuda.synchronize()
     return (perm.cpu().numpy(), parent.cpu().numpy(), anc.cpu().numpy().view(np.uint64),
             status.cpu().numpy().view(np.uint32), tab.cpu().numpy(), plan)
@@ -103,11 +104,10 @@ def test_negative_device_prefix_writes_only_its_own_table_range():
     stay as they were) and the request is flagged."""
     wl, rp, rs, _ = _raw_batch([6, 8, 5], [20, 30, 40], seed=13)
     prefix = wl.prefix_len.copy()
-    prefix[1] = -3
-    wl2 = inputs.Workload(**{**wl.__dict__, "prefix_len": prefix})
+    prefix[1] = -3                        # on the device only; the plan has the real bound
     before = wl.slot_table.copy()
-    ref = ot.marshal(wl2.num_tree, rp, rs, prefix, wl.slot_indptr, before)
-    got = _gpu_marshal(wl2, rp, rs, before)
+    ref = ot.marshal(wl.num_tree, rp, rs, prefix, wl.slot_indptr, before)
+    got = _gpu_marshal(wl, rp, rs, before, device_prefix=prefix)
     assert got[3][1] & ot.BAD_TABLE and got[3][0] == 0 and got[3][2] == 0
     np.testing.assert_array_equal(got[4], ref[4])
     # request 0's range holds exactly what a run with a valid request 1 writes
