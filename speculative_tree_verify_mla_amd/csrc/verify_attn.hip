@@ -27,14 +27,15 @@
 //     copies go out as soon as its slot-table entries have landed, while Q
 //     is still in flight.
 //   - Tiles of 64 pool rows go straight from HBM into LDS with
-//     global_load_lds_dwordx4 (1 KB per wave instruction), double-buffered:
-//     one tile is in flight while the other is consumed.  The slot-table
-//     entries of a tile are copied into a small LDS ring two tiles ahead of
-//     its rows.  All these copies are inline asm counted by hand (see
-//     vm_wait), so the compiler never makes an LDS read wait for them.  The
-//     latent part of a row is stored with a 1072-byte pitch and the rope part
-//     XOR-swizzled, so both MFMA read patterns below are free of LDS bank
-//     conflicts.
+//     global_load_lds_dwordx4 (1 KB per wave instruction: one 128-byte line
+//     of 8 rows, each lane holding its row's address, so a copy costs three
+//     instructions), double-buffered: one tile is in flight while the other
+//     is consumed.  The slot-table entries of a tile are copied into a small
+//     LDS ring two tiles ahead of its rows.  All these copies are inline asm
+//     counted by hand (see vm_wait), so the compiler never makes an LDS read
+//     wait for them.  In LDS a tile is stored line by line with the 16-byte
+//     pieces of each row XOR-swizzled (piece_off), so both MFMA read patterns
+//     below are free of LDS bank conflicts.
 //   - S^T[key][row] = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K fragment
 //     from LDS, B = Q rows held in accumulation registers).  The output layout gives each lane
 //     one query row (lane % 32) and, per register quad, 4 of the wave's keys,
@@ -68,6 +69,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 
 #include "verify_attn.h"
 
@@ -81,17 +83,19 @@ constexpr int HALF = TILE / 2;    // keys of a tile one wave owns (the MFMA M di
 constexpr int SPLIT_ALIGN = 32;   // split lengths are multiples of this many keys
 constexpr int THREADS = 256;      // 4 waves, one per SIMD
 constexpr int ROWS = 64;          // query rows per work item
-constexpr int LAT_STRIDE = DV + 24;               // bf16 per latent row in LDS (1072 B)
-constexpr int LAT_ELEMS = TILE * LAT_STRIDE;
-constexpr int BUF_ELEMS = LAT_ELEMS + TILE * DROPE;  // one tile buffer: 76,800 B
+constexpr int NPIECE = DQK / 8;                   // 16-byte pieces of a key row: 64 latent, 8 rope
+constexpr int NLINE = NPIECE / 8;                 // 128-byte lines of a key row: 8 latent, 1 rope
+constexpr int CHUNK = 8 * 128;                    // one line of 8 keys (one copy instruction)
+constexpr int LINE = (TILE / 8) * CHUNK;          // one line of all the keys of a tile
+constexpr int BUF_BYTES = NLINE * LINE;           // one tile buffer: 73,728 B
+constexpr int BUF_ELEMS = BUF_BYTES / 2;
 constexpr int QK_STEPS = DQK / 16;   // 36 MFMA k-steps (16 columns each) for the score
 constexpr int LAT_STEPS = DV / 16;   // the first 32 are latent columns, the last 4 rope
 constexpr int O_BLK = DV / 32;       // 16 MFMA column blocks (32 columns) of the output
 constexpr int O_HALF = O_BLK / 2;    // 8 of them per wave (one column half)
 constexpr int PART_VEC = ROWS * DV / 4;  // 4-column entries of one work item's partial output
 constexpr int SLOT_RING = 4;         // LDS ring of per-tile slot-table entries (3 live)
-constexpr int LAT_DMA = TILE / 4;    // latent rows one wave copies per tile
-constexpr int ROPE_DMA = TILE / 32;  // rope blocks (8 keys each) one wave copies per tile
+constexpr int COPIES = 2 * NLINE;    // copies one wave issues per tile: 9 lines of 2 key groups
 constexpr int MIN_KEYS_PER_SPLIT = 128;
 constexpr float REF_SLACK = 64.f;  // log2 units: probabilities stay <= 2^64
 constexpr float LOG2E = 1.4426950408889634f;
@@ -185,29 +189,48 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_base) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// 16 bytes per lane from sbase + voff (lane i writes lds + 16 i)
-__device__ __forceinline__ void dma16_s(uint32_t lds, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-// 16 bytes per lane from a per-lane address
-__device__ __forceinline__ void dma16_v(uint32_t lds, const void* addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-               :: "s"(lds), "v"(addr) : "memory", "m0");
-}
-// the same two copies without the streaming hint, for data every block reads
-__device__ __forceinline__ void dma16_s_keep(uint32_t lds, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_v_keep(uint32_t lds, const void* addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(addr) : "memory", "m0");
-}
 // 4 bytes per lane from a per-lane address (lane i writes lds + 4 i)
 __device__ __forceinline__ void dma4_v(uint32_t lds, const void* addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds), "v"(addr) : "memory", "m0");
+}
+// Copy of line J of key group 2 w + E (w = wave) of a tile: the lane's
+// address (addr) points at its key row's piece (lane % 8) ^ swz(key) of line
+// 0; lds_w = tile buffer + 2 w CHUNK.  The instruction offset 128 J advances
+// both the global address (by one line) and the LDS address, so
+// m0 = lds_w + E CHUNK + (LINE - 128) J puts lane l at
+// buffer + J LINE + (2 w + E) CHUNK + 16 l.
+template <int E, int J>
+__device__ __forceinline__ void dma_line(uint32_t lds_w, const void* addr) {
+  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3 nt"
+               :: "s"(lds_w), "v"(addr), "n"(E * CHUNK + (LINE - 128) * J), "n"(128 * J)
+               : "memory", "m0", "scc");
+}
+template <int E, int J>
+__device__ __forceinline__ void dma_line_keep(uint32_t lds_w, const void* addr) {
+  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3"
+               :: "s"(lds_w), "v"(addr), "n"(E * CHUNK + (LINE - 128) * J), "n"(128 * J)
+               : "memory", "m0", "scc");
+}
+// all 18 copies of a wave (addr[e]: key group 2 w + e)
+template <int... J>
+__device__ __forceinline__ void dma_lines_keep(uint32_t lds_w, const void* addr0, const void* addr1,
+                                               std::integer_sequence<int, J...>) {
+  (dma_line_keep<0, J>(lds_w, addr0), ...);
+  (dma_line_keep<1, J>(lds_w, addr1), ...);
+}
+// copy C of a wave's 18: key group 2 w + C / 9, line C % 9
+template <int C>
+__device__ __forceinline__ void dma_copy(uint32_t lds_w, const void* addr0, const void* addr1) {
+  if (C < NLINE) dma_line<0, C % NLINE>(lds_w, addr0);
+  else dma_line<1, C % NLINE>(lds_w, addr1);
+}
+// copies 2 part and 2 part + 1 (part is a constant once the caller's loop is unrolled)
+template <int... P>
+__device__ __forceinline__ void dma_part(int part, uint32_t lds_w, const void* addr0,
+                                         const void* addr1, std::integer_sequence<int, P...>) {
+  ((part == P ? (dma_copy<2 * P>(lds_w, addr0, addr1), dma_copy<2 * P + 1>(lds_w, addr0, addr1))
+              : void()), ...);
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -237,10 +260,17 @@ __device__ __forceinline__ int32_t table_entry(const int32_t* __restrict__ table
   return table[k < k_end ? k : k_end - 1];
 }
 
-// Rope columns of a key row are stored as 8 pieces of 16 bytes whose order
-// is XOR-swizzled by the key index, spreading 16 consecutive keys over all
-// LDS banks for the score MFMA reads.
-__device__ __forceinline__ int rope_piece(int key, int piece) { return piece ^ ((key >> 1) & 7); }
+// LDS tile layout: piece p (columns 8p .. 8p+7, 16 bytes) of key k lies at
+//   (p / 8) LINE + (k / 8) CHUNK + (k % 8) 128 + ((p % 8) ^ swz(k)) 16.
+// A copy instruction moves one 128-byte line of 8 keys (8 lanes per key, one
+// global line each).  swz keeps the score reads (one piece of 16
+// consecutive keys) and the transposed value reads (4 pieces of 4 keys) on
+// distinct LDS banks.
+__device__ __forceinline__ constexpr int swz(int k) { return (((k >> 1) & 1) << 2) | ((k >> 2) & 3); }
+// byte offset of piece p of key k within a tile buffer
+__device__ __forceinline__ constexpr int piece_off(int k, int p) {
+  return (p >> 3) * LINE + (k >> 3) * CHUNK + (k & 7) * 128 + (((p & 7) ^ swz(k)) << 4);
+}
 
 // Which keys a launch of the partial kernel covers.
 //   FUSED:  every split of a request covers a slice of its L + T keys; tiles
@@ -255,7 +285,7 @@ __device__ __forceinline__ int rope_piece(int key, int piece) { return piece ^ (
 // is the same for both.
 enum KernelMode { FUSED = 0, PREFIX = 1, TREE = 2 };
 
-// LDS of one work item (163,344 bytes of the 160 KB).
+// LDS of one work item (157,200 bytes of the 160 KB).
 struct PartialSmem {
   __attribute__((aligned(16))) uint16_t tiles[2 * BUF_ELEMS];
   // bf16 probabilities [row half][key half][lane] (two value-MFMA operands per
@@ -397,75 +427,64 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   // fragments per wave).  Rows past the group's end copy row 0 of the
   // request: they repeat its scores exactly (so raise no restart of their
   // own) and their partial rows are never merged.  Wave w copies rows
-  // 16w .. 16w+15.  The first tile goes into the first buffer; the second
-  // tile's copies start after the barrier at the top of the first tile,
-  // when every wave has read its fragments.
+  // 16w .. 16w+15.  The first tile goes into the first buffer;
+  // the second tile's copies start after the barrier at the top of the
+  // first tile, when every wave has read its fragments.
   {
     const uint16_t* const q0 = a.q + (int64_t)a.tree_begin[r] * H * DQK;
-    const int g0 = g * ROWS;
-    const uint32_t qbuf = lds_addr(tiles + BUF_ELEMS);
+    const uint16_t* src[2];
 #pragma unroll
-    for (int c = 0; c < LAT_DMA; ++c) {
-      const int i = wave * LAT_DMA + c;
-      const int rr = g0 + i < rows_r ? g0 + i : 0;
-      dma16_s_keep(qbuf + i * (LAT_STRIDE * 2), q0 + (int64_t)rr * DQK, lane * 16);
+    for (int e = 0; e < 2; ++e) {
+      const int i = 16 * wave + 8 * e + (lane >> 3);   // row of the group this lane copies
+      const int rr = g * ROWS + i < rows_r ? g * ROWS + i : 0;
+      src[e] = q0 + (int64_t)rr * DQK + 8 * ((lane & 7) ^ swz(i));
     }
-#pragma unroll
-    for (int j = 0; j < ROPE_DMA; ++j) {
-      const int kb = (wave * ROPE_DMA + j) * 8;
-      const int i = kb + (lane >> 3);
-      const int rr = g0 + i < rows_r ? g0 + i : 0;
-      dma16_v_keep(qbuf + (LAT_ELEMS + kb * DROPE) * 2,
-                   q0 + (int64_t)rr * DQK + DV + rope_piece(i, lane & 7) * 8);
-    }
+    dma_lines_keep(lds_addr(tiles + BUF_ELEMS) + 2 * wave * CHUNK, src[0], src[1],
+                   std::make_integer_sequence<int, NLINE>{});
   }
 
-  // ---- tile loader.  For tile u, lane l takes the slot of key l from the
-  // ring; wave w copies the latent rows of keys 16w .. 16w+15 (one 1 KB copy
-  // each) and the rope parts of the same keys (two copies of 8 rows).  Keys
-  // past the split end and slots outside the pool copy the zero row.
+  // ---- tile loader.  Wave w copies the 9 lines of keys 16w .. 16w+15 (18
+  // copies of 1 KB: 8 keys x 128 bytes); lane l takes key 16w + 8e + l/8
+  // (e = 0, 1), whose slot it reads from the ring.  Keys past the split end
+  // and slots outside the pool copy the zero row.
   uint32_t bad = 0u;
-  // The copies of a tile are issued in 9 pieces of 2 spread over the score
+  // The copies of a tile are issued in 9 parts of 2 spread over the score
   // MFMAs of the previous tile: a burst of all of them stalls the wave on
   // memory back-pressure while the MFMA pipe idles.
   struct TileIssue {
-    int32_t vslot;   // slot of key `lane` of the tile
-    uint64_t use;    // bit j: key j is read (exists and its slot is in the pool)
-    uint32_t lbuf;   // LDS byte address of the tile buffer
+    const uint16_t* src[2];   // this lane's piece of line 0 of its two key rows
+    uint32_t lds_w;           // LDS byte address of chunk 2 w of the tile buffer
   };
-  // vslot: sring[u % SLOT_RING][lane], read ahead by the caller
-  auto prepare_tile = [&](int u, int32_t vslot, uint16_t* buf) -> TileIssue {
+  struct SlotPair {
+    int32_t v[2];
+  };
+  auto read_slots = [&](int u) -> SlotPair {
+    SlotPair sp;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) sp.v[e] = sring[u & (SLOT_RING - 1)][16 * wave + 8 * e + (lane >> 3)];
+    return sp;
+  };
+  // vslot: read_slots(u), read ahead by the caller
+  auto prepare_tile = [&](int u, const SlotPair& vslot, uint16_t* buf) -> TileIssue {
     TileIssue ti;
-    ti.vslot = vslot;
-    const int k = k0 + u * TILE + lane;
-    const bool exists = k < k1;
-    const bool inside = ti.vslot >= 0 && (int64_t)ti.vslot < a.num_slots;
-    if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
-    ti.use = __ballot(exists && inside);
-    ti.lbuf = lds_addr(buf);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = 16 * wave + 8 * e + (lane >> 3);
+      const int k = k0 + u * TILE + key;
+      const bool exists = k < k1;
+      const bool inside = vslot.v[e] >= 0 && (int64_t)vslot.v[e] < a.num_slots;
+      if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
+      ti.src[e] = (exists && inside ? a.kv + (int64_t)vslot.v[e] * a.stride : va_zero_row) +
+                  8 * ((lane & 7) ^ swz(key));
+    }
+    ti.lds_w = lds_addr(buf) + 2 * wave * CHUNK;
     return ti;
   };
-  // copies 2*part, 2*part+1 of the tile: 0..15 latent rows, 16..17 rope blocks
+  // copies 2 part, 2 part + 1 of the tile
   auto issue_part = [&](const TileIssue& ti, int part) {
-#pragma unroll
-    for (int c = 2 * part; c < 2 * part + 2; ++c) {
-      if (c < LAT_DMA) {
-        const int key = wave * LAT_DMA + c;
-        const int32_t sj = __builtin_amdgcn_readlane(ti.vslot, key);
-        const uint64_t ok = 0ull - ((ti.use >> key) & 1ull);   // all ones when the row is read
-        const uint64_t row = ((uint64_t)(a.kv + (int64_t)sj * a.stride) & ok) |
-                             ((uint64_t)va_zero_row & ~ok);
-        dma16_s(ti.lbuf + key * (LAT_STRIDE * 2), (const void*)row, lane * 16);
-      } else {
-        const int kb = (wave * ROPE_DMA + (c - LAT_DMA)) * 8;   // first key of this rope block
-        const int key = kb + (lane >> 3);                        // key of this lane
-        const int32_t sk = __shfl(ti.vslot, key);
-        const uint16_t* row = ((ti.use >> key) & 1ull) ? a.kv + (int64_t)sk * a.stride : va_zero_row;
-        dma16_v(ti.lbuf + (LAT_ELEMS + kb * DROPE) * 2, row + DV + rope_piece(key, lane & 7) * 8);
-      }
-    }
+    dma_part(part, ti.lds_w, ti.src[0], ti.src[1], std::make_integer_sequence<int, COPIES / 2>{});
   };
-  static_assert(LAT_DMA + ROPE_DMA == 2 * 9, "copies of a tile = 2 per score MFMA group");
+  static_assert(COPIES == 2 * 9, "copies of a tile = 2 per score MFMA group");
 
 
   f32x16 o[O_HALF];
@@ -482,15 +501,25 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   float l_run = 0.f;
   float lb_run = 0.f;
 
-  // per-lane LDS element offsets of the MFMA operands within a tile buffer
+  // per-lane LDS byte offsets of the MFMA operands within a tile buffer.
+  // Score k-step k reads piece 2k + lh of key krow: LINE (k / 4) + kb[k % 4].
   const int krow = kh * HALF + lrow;                      // this lane's key row for the score
-  const int k_lat = krow * LAT_STRIDE + lh * 8;           // K fragment, latent k-steps
-  const int k_rope = LAT_ELEMS + krow * DROPE;            // K fragment row, rope k-steps 32..35
+  uint32_t kb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kb[i] = piece_off(krow, 2 * i + lh);
   // value operand: block b = lane/16 reads keys 16*ks + 4*(b>>1) + i/4 (+8)
   // and columns 16*(b&1) + 4*(i%4) of each 32-column block (i = lane%16) of
   // this wave's column half
-  const int v_off = (4 * lh + ((lane & 15) >> 2)) * LAT_STRIDE + 16 * ((lane >> 4) & 1) +
-                    4 * (lane & 3) + kh * (O_HALF * 32);
+  // (key 16 ks' + 8n + 4 (b>>1) + i/4, piece 32 kh + 4 cb + 2 (b&1) + (i%4)/2,
+  // byte 8 (i%2): vb[cb % 2][n] below, plus LINE (4 kh + cb / 2) and 2 CHUNK ks')
+  uint32_t vb[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      vb[c][n] = piece_off(8 * n + 4 * lh + ((lane & 15) >> 2),
+                           4 * c + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + (lane & 1) * 8;
+  }
   const int qkey = kh * HALF + 4 * lh;   // tile key of register 4*qd+i is qkey + 8*qd + i
 
   // Consumes tile t (one buffer).  `first` is set on the first tile of a
@@ -515,9 +544,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
 #pragma unroll
       for (int kk = 0; kk < QG; ++kk) {
         const int k = k0s + kk;
-        const int off = k < LAT_STEPS ? k_lat + k * 16
-                                      : k_rope + rope_piece(krow, 2 * (k - LAT_STEPS) + lh) * 8;
-        kf[kk] = *reinterpret_cast<const bf16x8*>(buf + off);
+        kf[kk] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(buf) +
+                                                  LINE * (k >> 2) + kb[k & 3]);
       }
     };
     // after each group's MFMAs, 2 of the next tile's copies
@@ -602,9 +630,10 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     auto load_v2 = [&](bf16x8* vf, int cb) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint16_t* p0 = buf + v_off + (2 * half + j) * 16 * LAT_STRIDE + cb * 32;
-        const i16x4 v0 = lds_read_tr16(p0);
-        const i16x4 v1 = lds_read_tr16(p0 + 8 * LAT_STRIDE);
+        const uint8_t* p0 = reinterpret_cast<const uint8_t*>(buf) + (4 * kh + (cb >> 1)) * LINE +
+                            (2 * half + j) * (2 * CHUNK);
+        const i16x4 v0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(p0 + vb[cb & 1][0]));
+        const i16x4 v1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(p0 + vb[cb & 1][1]));
         const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         vf[j] = __builtin_bit_cast(bf16x8, v8);
       }
@@ -666,12 +695,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       __syncthreads();   // slots 0, 1 and restart_sh ready
     } else {
       // wave 0's slot and parent entries went out before its 18 Q copies
-      vm_wait<LAT_DMA + ROPE_DMA>();
+      vm_wait<COPIES>();
       __syncthreads();   // slots 0, 1, parents, status_sh and restart_sh ready
     }
     if (ntiles > 0) {
       // tile 0 goes out without waiting for Q, which fills the other buffer
-      const TileIssue first_tile = prepare_tile(0, sring[0][lane], tiles);
+      const TileIssue first_tile = prepare_tile(0, read_slots(0), tiles);
 #pragma unroll
       for (int g = 0; g < 9; ++g) issue_part(first_tile, g);
       issue_slots(2);
@@ -697,28 +726,25 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       }
       // this wave's Q copies precede its tile-0 copies (and wave 0's slot copy)
       if (ntiles > 0) {
-        if (wave == 0) vm_wait<LAT_DMA + ROPE_DMA + 1>();
-        else vm_wait<LAT_DMA + ROPE_DMA>();
+        if (wave == 0) vm_wait<COPIES + 1>();
+        else vm_wait<COPIES>();
       } else {
         vm_wait<0>();
       }
       __syncthreads();   // Q and anc[] ready
       if (MODE != PREFIX) anc_row = row_ok ? anc[rho / H] : 0ull;
-      const uint16_t* const qb = tiles + BUF_ELEMS;
+      const uint8_t* const qb = reinterpret_cast<const uint8_t*>(tiles + BUF_ELEMS);
       const int qr = rh * HALF + lrow;
 #pragma unroll
-      for (int k = 0; k < QK_STEPS; ++k) {
-        const int off = k < LAT_STEPS ? qr * LAT_STRIDE + lh * 8 + k * 16
-                                      : LAT_ELEMS + qr * DROPE + rope_piece(qr, 2 * (k - LAT_STEPS) + lh) * 8;
-        qf[k] = *reinterpret_cast<const bf16x8*>(qb + off);
-      }
+      for (int k = 0; k < QK_STEPS; ++k)
+        qf[k] = *reinterpret_cast<const bf16x8*>(qb + piece_off(qr, 2 * k + lh));
     }
 
     bool restart = false;
     bool restart_seen = false;   // restart_sh as of the last mid-tile barrier
     // slots of tile 1 (landed before the barrier above); each iteration reads
     // the slots of the tile after next, which landed at its top wait
-    int32_t vslot_next = sring[1][lane];
+    SlotPair vslot_next = read_slots(1);
     for (int t = 0; t < ntiles; ++t) {
       vm_wait<0>();
       lds_barrier();   // tile t is in LDS; every wave is done with tile t-1
@@ -729,7 +755,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
       // the next tile's copies; after the last tile they copy the zero row
       // (every key lies past the split end) into the free buffer
       const TileIssue nxt = prepare_tile(t + 1, vslot_next, tiles + ((t + 1) & 1) * BUF_ELEMS);
-      vslot_next = sring[(t + 2) & (SLOT_RING - 1)][lane];
+      vslot_next = read_slots(t + 2);
       issue_slots(t + 3);
       compute(t, tiles + (t & 1) * BUF_ELEMS, anc_row, t == 0, nxt, sweep);
       if (!sweep) value_half(tiles + (t & 1) * BUF_ELEMS, kh, pown);
@@ -988,27 +1014,18 @@ __global__ __launch_bounds__(STREAM_THREADS) void va_stream_read_kernel(const u3
 __global__ __launch_bounds__(64) void va_gather_kernel(const uint16_t* kv, int64_t num_slots,
                                                        int32_t stride, const int32_t* table,
                                                        int32_t n, uint16_t* dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t row_lds[LAT_STRIDE + DROPE];
+  __shared__ __attribute__((aligned(16))) uint16_t row_lds[DQK];
   const int k = blockIdx.x;
   const int lane = threadIdx.x;
   const int32_t slot = table_entry(table, k, n);
   const bool inside = slot >= 0 && (int64_t)slot < num_slots;
   const uint16_t* row = inside ? kv + (int64_t)slot * stride : va_zero_row;
-  dma16(row + lane * 8, row_lds);
-  if (lane < 8) {
-    // same rope path as the partial pass, for key index 0 of a tile
-    dma16(row + DV + rope_piece(0, lane) * 8, row_lds + LAT_STRIDE);
-  }
+  dma16(row + lane * 8, row_lds);                        // latent pieces 0..63
+  if (lane < NPIECE - 64) dma16(row + DV + lane * 8, row_lds + DV);   // rope pieces 64..71
   wait_vmcnt<0>();
   __syncthreads();
   for (int i = lane; i < DQK / 8; i += 64) {
-    u32x4 v;
-    if (i < DV / 8) {
-      v = *reinterpret_cast<const u32x4*>(row_lds + i * 8);
-    } else {
-      const int piece = i - DV / 8;
-      v = *reinterpret_cast<const u32x4*>(row_lds + LAT_STRIDE + rope_piece(0, piece) * 8);
-    }
+    u32x4 v = *reinterpret_cast<const u32x4*>(row_lds + i * 8);
     if (!inside) v = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
     *reinterpret_cast<u32x4*>(dst + (int64_t)k * DQK + i * 8) = v;
   }

@@ -160,6 +160,17 @@ def test_split_count_does_not_change_the_result(nsplit, monkeypatch):
     check(wl, out, lse, what=f"nsplit {nsplit}")
 
 
+def test_split_of_draft_keys_only(monkeypatch):
+    """L = 1024, T = 64, 9 splits: the last split holds the 64 draft keys
+    alone, and with a star tree node j sees only key L + j there (and all of
+    the prefix elsewhere).  Every row still counts its own key."""
+    monkeypatch.setenv("VA_NSPLIT", "9")
+    wl = inputs.make_workload("draft_split", 4, [64], [1024], 4096, seed=71, tree="star")
+    out, lse, status, plan = run_gpu(wl)
+    assert status == 0 and plan.splits() == [9]
+    check(wl, out, lse, what="draft-only split, star tree")
+
+
 def test_graph_bound_above_actual_prefix():
     """Plan with an upper bound, run with a shorter device prefix length."""
     wl = inputs.make_workload("bound", 8, [16], [3000], 8192, seed=5)
