@@ -216,6 +216,40 @@ int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out
                        va_stream_t stream);
 
 /*
+ * verify_attn_forward_static - verify_attn_run followed by verify_attn_reduce
+ * (the same kernels, enqueued back to back on `stream`) with the partials in
+ * a scratch array the library holds on each device for the life of the
+ * process, so the call allocates nothing and takes no workspace.  For callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments as verify_attn_run and verify_attn_reduce; out and lse as
+ * verify_attn_reduce.  The scratch holds VA_STATIC_SCRATCH_BYTES, enough for
+ * VA_STATIC_SCRATCH_WORK work items (any plan with plan->total_work <= 256,
+ * e.g. every single-request plan for up to 256 compute units); a plan whose
+ * workspace_bytes exceeds it is refused with VA_ERR_WORKSPACE.
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, with the device current); no call allocates.
+ * Every call on one device shares its array: calls whose kernels may
+ * overlap on one device (different streams without ordering) race and must
+ * be serialised by the caller.  The kernels write every scratch word they
+ * read in the same call, so nothing needs clearing between calls.  The
+ * status words stay in the scratch: rows of a request that failed the
+ * device checks come out as NaN in out and lse, as with verify_attn_reduce.
+ * Errors: VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_SHAPE, VA_ERR_ALIGN,
+ *         VA_ERR_WORKSPACE (plan too large for the scratch), VA_ERR_HIP.
+ */
+#define VA_STATIC_SCRATCH_WORK 256
+/* 256 work items x (65,536 B partials + 512 B lse pairs) + 1,024 B status words */
+#define VA_STATIC_SCRATCH_BYTES 16909312
+int verify_attn_forward_static(const va_plan* plan, const uint16_t* q, const uint16_t* kv_pool,
+                               int64_t num_slots, int32_t kv_row_stride,
+                               const int32_t* slot_table, int32_t slot_table_len,
+                               const int32_t* slot_indptr, const int32_t* prefix_len,
+                               const int32_t* parent, float sm_scale, uint16_t* out, float* lse,
+                               va_stream_t stream);
+
+/*
  * verify_attn_read_status - OR of the device status words the last run wrote
  * (VA_STATUS_* bits) into *h_status.  Diagnostic: it copies to the host and
  * synchronises `stream`, so it must not be called under graph capture.

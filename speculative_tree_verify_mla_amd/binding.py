@@ -38,7 +38,7 @@ STATUS_BITS = {1: "BAD_PREFIX", 2: "SHORT_TABLE", 4: "BAD_SLOT", 8: "BAD_PARENT"
 # Every symbol include/verify_attn.h declares.
 EXPORTS = (
     "verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
-    "verify_attn_read_status",
+    "verify_attn_forward_static", "verify_attn_read_status",
     "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_stream_read",
     "verify_attn_error_string",
     "verify_attn_plan_struct_size", "verify_attn_compact_workspace_bytes", "verify_attn_compact",
@@ -98,6 +98,8 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_run.argtypes = [ctypes.POINTER(VaPlan), P, P, i64, i32, P, i32, P, P, P, f32,
                                     P, sz, P]
     lib.verify_attn_reduce.argtypes = [ctypes.POINTER(VaPlan), P, P, P, P]
+    lib.verify_attn_forward_static.argtypes = [ctypes.POINTER(VaPlan), P, P, i64, i32, P, i32, P,
+                                               P, P, f32, P, P, P]
     lib.verify_attn_read_status.argtypes = [ctypes.POINTER(VaPlan), P, P,
                                             ctypes.POINTER(ctypes.c_uint32)]
     lib.verify_attn_check_tree.argtypes = [P, i32]
@@ -114,7 +116,7 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_plan_struct_size.argtypes = []
     lib.verify_attn_plan_struct_size.restype = sz
     for name in ("verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
-                 "verify_attn_read_status", "verify_attn_check_tree", "verify_attn_gather_rows",
+                 "verify_attn_forward_static", "verify_attn_read_status", "verify_attn_check_tree", "verify_attn_gather_rows",
                  "verify_attn_stream_read"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.verify_attn_plan_struct_size() != ctypes.sizeof(VaPlan):
@@ -180,13 +182,7 @@ def verify_attn_plan(num_heads, prefix_len, num_tree, num_cus=0, split_tree=Fals
     return plan
 
 
-def verify_attn_run(plan, q, kv_pool, slot_table, slot_indptr, prefix_len, parent, sm_scale,
-                    workspace, stream=None):
-    """Enqueue the partial pass.  Tensors: q/kv_pool bf16 (or 16-bit ints),
-    tables int32, workspace uint8 of at least plan.workspace_bytes."""
-    import torch
-    b16 = _bf16_types()
-    i32 = (torch.int32,)
+def _check_run_tensors(plan, q, kv_pool, slot_indptr, prefix_len, parent):
     B = int(plan.num_requests)
     if tuple(q.shape) != (int(plan.total_tree), int(plan.num_heads), VA_D_QK):
         raise ValueError(f"q must be [{plan.total_tree}, {plan.num_heads}, 576], got {tuple(q.shape)}")
@@ -194,10 +190,20 @@ def verify_attn_run(plan, q, kv_pool, slot_table, slot_indptr, prefix_len, paren
         raise ValueError("kv_pool must be [num_slots, >=576]")
     if kv_pool.stride(1) != 1:
         raise ValueError("kv_pool rows must be contiguous")
-    if not kv_pool.is_cuda or kv_pool.dtype not in b16:
+    if not kv_pool.is_cuda or kv_pool.dtype not in _bf16_types():
         raise TypeError("kv_pool must be a bf16 device tensor")
     if slot_indptr.numel() < B + 1 or prefix_len.numel() < B or parent.numel() < plan.total_tree:
         raise ValueError("slot_indptr / prefix_len / parent are shorter than the plan needs")
+
+
+def verify_attn_run(plan, q, kv_pool, slot_table, slot_indptr, prefix_len, parent, sm_scale,
+                    workspace, stream=None):
+    """Enqueue the partial pass.  Tensors: q/kv_pool bf16 (or 16-bit ints),
+    tables int32, workspace uint8 of at least plan.workspace_bytes."""
+    import torch
+    b16 = _bf16_types()
+    i32 = (torch.int32,)
+    _check_run_tensors(plan, q, kv_pool, slot_indptr, prefix_len, parent)
     kv_ptr = ctypes.c_void_p(kv_pool.data_ptr())
     rc = load_library().verify_attn_run(
         ctypes.byref(plan), _dptr(q, b16, "q"), kv_ptr, int(kv_pool.shape[0]),
@@ -220,6 +226,27 @@ def verify_attn_reduce(plan, workspace, out, lse, stream=None):
         _dptr(out, _bf16_types(), "out"), _dptr(lse, (torch.float32,), "lse"),
         _stream_handle(stream))
     _check("verify_attn_reduce", rc)
+
+
+def verify_attn_forward_static(plan, q, kv_pool, slot_table, slot_indptr, prefix_len, parent,
+                               sm_scale, out, lse, stream=None):
+    """Partial pass and merge in one call, with the partials in the library's
+    per-device scratch (no workspace, nothing allocated).  Arguments as
+    verify_attn_run and verify_attn_reduce."""
+    import torch
+    b16 = _bf16_types()
+    i32 = (torch.int32,)
+    _check_run_tensors(plan, q, kv_pool, slot_indptr, prefix_len, parent)
+    rows = int(plan.total_tree) * int(plan.num_heads)
+    if out.numel() != rows * VA_D_V or lse.numel() != rows:
+        raise ValueError(f"out must hold {rows}x512 and lse {rows} elements")
+    rc = load_library().verify_attn_forward_static(
+        ctypes.byref(plan), _dptr(q, b16, "q"), ctypes.c_void_p(kv_pool.data_ptr()),
+        int(kv_pool.shape[0]), int(kv_pool.stride(0)), _dptr(slot_table, i32, "slot_table"),
+        int(slot_table.numel()), _dptr(slot_indptr, i32, "slot_indptr"),
+        _dptr(prefix_len, i32, "prefix_len"), _dptr(parent, i32, "parent"), float(sm_scale),
+        _dptr(out, b16, "out"), _dptr(lse, (torch.float32,), "lse"), _stream_handle(stream))
+    _check("verify_attn_forward_static", rc)
 
 
 def verify_attn_read_status(plan, workspace, stream=None) -> int:

@@ -69,9 +69,17 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <utility>
 
 #include "verify_attn.h"
+
+// Scratch of verify_attn_forward_static: the partials, lse pairs and status
+// words of up to VA_STATIC_SCRATCH_WORK work items, laid out as a workspace.
+// Each device holds its own copy for the life of the process.  Host code
+// takes its device address from hipGetSymbolAddress (static_scratch below)
+// and never passes the name itself to a kernel.
+static __device__ __align__(256) unsigned char scratch[VA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -1080,6 +1088,129 @@ bool plan_ok(const va_plan* p) {
          p->workspace_bytes == o_bytes + lse_bytes + st_bytes;
 }
 
+// Checks of the launch arguments verify_attn_run and verify_attn_forward_static share.
+int check_run_args(const va_plan* plan, const uint16_t* q, const uint16_t* kv_pool,
+                   int64_t num_slots, int32_t kv_row_stride, const int32_t* slot_table,
+                   int32_t slot_table_len, const int32_t* slot_indptr, const int32_t* prefix_len,
+                   const int32_t* parent, float sm_scale) {
+  if (plan == nullptr || q == nullptr || kv_pool == nullptr || slot_table == nullptr ||
+      slot_indptr == nullptr || prefix_len == nullptr || parent == nullptr)
+    return VA_ERR_NULL;
+  if (!plan_ok(plan)) return VA_ERR_PLAN;
+  if (num_slots < 1 || num_slots > (int64_t)INT32_MAX + 1 || kv_row_stride < DQK ||
+      slot_table_len < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return VA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(kv_pool) || (kv_row_stride % 8) != 0) return VA_ERR_ALIGN;
+  return VA_OK;
+}
+
+// The partial pass into workspace ws (checked by the caller).
+int launch_partial(const va_plan* plan, const uint16_t* q, const uint16_t* kv_pool,
+                   int64_t num_slots, int32_t kv_row_stride, const int32_t* slot_table,
+                   int32_t slot_table_len, const int32_t* slot_indptr, const int32_t* prefix_len,
+                   const int32_t* parent, float sm_scale, char* ws, hipStream_t st) {
+  PartialArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q;
+  a.kv = kv_pool;
+  a.num_slots = num_slots;
+  a.stride = kv_row_stride;
+  a.num_requests = plan->num_requests;
+  a.num_heads = plan->num_heads;
+  a.total_work = plan->total_work;
+  a.scale_log2 = sm_scale * LOG2E;
+  a.slot_table = slot_table;
+  a.slot_table_len = slot_table_len;
+  a.slot_indptr = slot_indptr;
+  a.prefix_len = prefix_len;
+  a.parent = parent;
+  a.part_o = reinterpret_cast<uint32_t*>(ws);
+  a.part_lse = reinterpret_cast<float*>(ws + plan->lse_offset);
+  a.status = reinterpret_cast<uint32_t*>(ws + plan->status_offset);
+  for (int r = 0; r < plan->num_requests; ++r) {
+    a.num_tree[r] = plan->num_tree[r];
+    a.max_prefix[r] = plan->max_prefix[r];
+    a.nsplit[r] = plan->nsplit[r];
+    a.num_groups[r] = plan->num_groups[r];
+  }
+  for (int r = 0; r <= plan->num_requests; ++r) {
+    a.tree_begin[r] = plan->tree_begin[r];
+    a.work_begin[r] = plan->work_begin[r];
+  }
+  const unsigned grid = 8u * (unsigned)((plan->total_work + 7) / 8);   // see the XCD work order
+  if (plan->mode == VA_MODE_SPLIT_TREE) {
+    int tree_blocks = 0;
+    for (int r = 0; r < plan->num_requests; ++r) tree_blocks += plan->num_groups[r];
+    hipLaunchKernelGGL(va_split_kernel, dim3(grid + (unsigned)tree_blocks), dim3(THREADS), 0, st,
+                       a, tree_blocks);
+  } else {
+    hipLaunchKernelGGL(va_partial_kernel, dim3(grid), dim3(THREADS), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+// The merge of the partials in workspace ws (checked by the caller).
+int launch_reduce(const va_plan* plan, const char* ws, uint16_t* out, float* lse, hipStream_t st) {
+  ReduceArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.part_o = reinterpret_cast<const uint32_t*>(ws);
+  a.part_lse = reinterpret_cast<const float*>(ws + plan->lse_offset);
+  a.status = reinterpret_cast<const uint32_t*>(ws + plan->status_offset);
+  a.out = out;
+  a.lse = lse;
+  a.num_requests = plan->num_requests;
+  a.num_heads = plan->num_heads;
+  for (int r = 0; r < plan->num_requests; ++r) {
+    a.nsplit[r] = plan->nsplit[r];
+    a.num_groups[r] = plan->num_groups[r];
+  }
+  for (int r = 0; r <= plan->num_requests; ++r) {
+    a.tree_begin[r] = plan->tree_begin[r];
+    a.work_begin[r] = plan->work_begin[r];
+  }
+  int blocks = 0;
+  int max_ns = 1;
+  for (int r = 0; r < plan->num_requests; ++r) {
+    blocks += plan->num_groups[r] * RED_PIECES;
+    max_ns = max(max_ns, plan->nsplit[r]);
+  }
+  if (max_ns <= 16)
+    hipLaunchKernelGGL(va_reduce_kernel<16>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else if (max_ns <= 32)
+    hipLaunchKernelGGL(va_reduce_kernel<32>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else if (max_ns <= 64)
+    hipLaunchKernelGGL(va_reduce_kernel<64>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else if (max_ns <= 128)
+    hipLaunchKernelGGL(va_reduce_kernel<128>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(va_reduce_kernel<VA_MAX_SPLITS>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept for the process.
+static_assert(VA_STATIC_SCRATCH_BYTES ==
+                  (int64_t)VA_STATIC_SCRATCH_WORK * (ROWS * DV * 2 + ROWS * 2 * 4) +
+                      ((VA_STATIC_SCRATCH_WORK * 4 + 255) & ~255),
+              "scratch = the workspace of VA_STATIC_SCRATCH_WORK work items");
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+int static_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return VA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return VA_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(scratch_ptr[dev]);
+  return VA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1205,58 +1336,15 @@ int verify_attn_run(const va_plan* plan, const uint16_t* q, const uint16_t* kv_p
                     int32_t slot_table_len, const int32_t* slot_indptr,
                     const int32_t* prefix_len, const int32_t* parent,
                     float sm_scale, void* workspace, size_t workspace_bytes, va_stream_t stream) {
-  if (plan == nullptr || q == nullptr || kv_pool == nullptr || slot_table == nullptr ||
-      slot_indptr == nullptr || prefix_len == nullptr || parent == nullptr)
-    return VA_ERR_NULL;
-  if (!plan_ok(plan)) return VA_ERR_PLAN;
-  if (num_slots < 1 || num_slots > (int64_t)INT32_MAX + 1 || kv_row_stride < DQK ||
-      slot_table_len < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
-    return VA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(kv_pool) || (kv_row_stride % 8) != 0) return VA_ERR_ALIGN;
+  const int rc = check_run_args(plan, q, kv_pool, num_slots, kv_row_stride, slot_table,
+                                slot_table_len, slot_indptr, prefix_len, parent, sm_scale);
+  if (rc != VA_OK) return rc;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
       (int64_t)workspace_bytes < plan->workspace_bytes)
     return VA_ERR_WORKSPACE;
-
-  PartialArgs a;
-  std::memset(&a, 0, sizeof a);
-  a.q = q;
-  a.kv = kv_pool;
-  a.num_slots = num_slots;
-  a.stride = kv_row_stride;
-  a.num_requests = plan->num_requests;
-  a.num_heads = plan->num_heads;
-  a.total_work = plan->total_work;
-  a.scale_log2 = sm_scale * LOG2E;
-  a.slot_table = slot_table;
-  a.slot_table_len = slot_table_len;
-  a.slot_indptr = slot_indptr;
-  a.prefix_len = prefix_len;
-  a.parent = parent;
-  char* ws = static_cast<char*>(workspace);
-  a.part_o = reinterpret_cast<uint32_t*>(ws);
-  a.part_lse = reinterpret_cast<float*>(ws + plan->lse_offset);
-  a.status = reinterpret_cast<uint32_t*>(ws + plan->status_offset);
-  for (int r = 0; r < plan->num_requests; ++r) {
-    a.num_tree[r] = plan->num_tree[r];
-    a.max_prefix[r] = plan->max_prefix[r];
-    a.nsplit[r] = plan->nsplit[r];
-    a.num_groups[r] = plan->num_groups[r];
-  }
-  for (int r = 0; r <= plan->num_requests; ++r) {
-    a.tree_begin[r] = plan->tree_begin[r];
-    a.work_begin[r] = plan->work_begin[r];
-  }
-  const unsigned grid = 8u * (unsigned)((plan->total_work + 7) / 8);   // see the XCD work order
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (plan->mode == VA_MODE_SPLIT_TREE) {
-    int tree_blocks = 0;
-    for (int r = 0; r < plan->num_requests; ++r) tree_blocks += plan->num_groups[r];
-    hipLaunchKernelGGL(va_split_kernel, dim3(grid + (unsigned)tree_blocks), dim3(THREADS), 0, st,
-                       a, tree_blocks);
-  } else {
-    hipLaunchKernelGGL(va_partial_kernel, dim3(grid), dim3(THREADS), 0, st, a);
-  }
-  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+  return launch_partial(plan, q, kv_pool, num_slots, kv_row_stride, slot_table, slot_table_len,
+                        slot_indptr, prefix_len, parent, sm_scale, static_cast<char*>(workspace),
+                        static_cast<hipStream_t>(stream));
 }
 
 int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out, float* lse,
@@ -1265,42 +1353,30 @@ int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out
     return VA_ERR_NULL;
   if (!plan_ok(plan)) return VA_ERR_PLAN;
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VA_ERR_ALIGN;
-  ReduceArgs a;
-  std::memset(&a, 0, sizeof a);
-  const char* ws = static_cast<const char*>(workspace);
-  a.part_o = reinterpret_cast<const uint32_t*>(ws);
-  a.part_lse = reinterpret_cast<const float*>(ws + plan->lse_offset);
-  a.status = reinterpret_cast<const uint32_t*>(ws + plan->status_offset);
-  a.out = out;
-  a.lse = lse;
-  a.num_requests = plan->num_requests;
-  a.num_heads = plan->num_heads;
-  for (int r = 0; r < plan->num_requests; ++r) {
-    a.nsplit[r] = plan->nsplit[r];
-    a.num_groups[r] = plan->num_groups[r];
-  }
-  for (int r = 0; r <= plan->num_requests; ++r) {
-    a.tree_begin[r] = plan->tree_begin[r];
-    a.work_begin[r] = plan->work_begin[r];
-  }
-  int blocks = 0;
-  int max_ns = 1;
-  for (int r = 0; r < plan->num_requests; ++r) {
-    blocks += plan->num_groups[r] * RED_PIECES;
-    max_ns = max(max_ns, plan->nsplit[r]);
-  }
+  return launch_reduce(plan, static_cast<const char*>(workspace), out, lse,
+                       static_cast<hipStream_t>(stream));
+}
+
+int verify_attn_forward_static(const va_plan* plan, const uint16_t* q, const uint16_t* kv_pool,
+                               int64_t num_slots, int32_t kv_row_stride,
+                               const int32_t* slot_table, int32_t slot_table_len,
+                               const int32_t* slot_indptr, const int32_t* prefix_len,
+                               const int32_t* parent, float sm_scale, uint16_t* out, float* lse,
+                               va_stream_t stream) {
+  int rc = check_run_args(plan, q, kv_pool, num_slots, kv_row_stride, slot_table,
+                          slot_table_len, slot_indptr, prefix_len, parent, sm_scale);
+  if (rc != VA_OK) return rc;
+  if (out == nullptr || lse == nullptr) return VA_ERR_NULL;
+  if (!aligned16(out)) return VA_ERR_ALIGN;
+  if (plan->workspace_bytes > (int64_t)VA_STATIC_SCRATCH_BYTES) return VA_ERR_WORKSPACE;
+  char* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc != VA_OK) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (max_ns <= 16)
-    hipLaunchKernelGGL(va_reduce_kernel<16>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else if (max_ns <= 32)
-    hipLaunchKernelGGL(va_reduce_kernel<32>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else if (max_ns <= 64)
-    hipLaunchKernelGGL(va_reduce_kernel<64>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else if (max_ns <= 128)
-    hipLaunchKernelGGL(va_reduce_kernel<128>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(va_reduce_kernel<VA_MAX_SPLITS>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+  rc = launch_partial(plan, q, kv_pool, num_slots, kv_row_stride, slot_table, slot_table_len,
+                      slot_indptr, prefix_len, parent, sm_scale, ws, st);
+  if (rc != VA_OK) return rc;
+  return launch_reduce(plan, ws, out, lse, st);
 }
 
 int verify_attn_read_status(const va_plan* plan, const void* workspace, va_stream_t stream,
