@@ -878,7 +878,9 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform: the split of each partial load, its address and its
+  // bounds test are scalar work
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int b = blockIdx.x;
   int r = 0;
   // block ranges: request r owns num_groups[r] * RED_PIECES blocks
@@ -898,20 +900,24 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   const int64_t wbase = (int64_t)a.work_begin[r] + g;   // work item of split s: wbase + s * G
 
   const int row = tid & 31;
-  const int sg = tid >> 5;
+  const int sg = tid >> 5;   // 2 wave + lane / 32
   const int prow = lane & 31;
+  // lse pair of split s: plse[s * lse_step] (s * lse_step < 2^31: at most
+  // 256 splits of at most 1024 row groups of 64 rows)
   const float2* plse = reinterpret_cast<const float2*>(a.part_lse) + wbase * ROWS + rh * 32 + row;
-  const u32x2* src = reinterpret_cast<const u32x2*>(a.part_o) + wbase * PART_VEC + piece * 64 + lane;
-  const int64_t lse_step = (int64_t)G * ROWS;
+  const int lse_step = G * ROWS;
+  const u32x2* src = reinterpret_cast<const u32x2*>(a.part_o) + wbase * PART_VEC + piece * 64;
   const int64_t split_step = (int64_t)G * PART_VEC;
   float2 lv[RED_LSE];
 #pragma unroll
   for (int i = 0; i < RED_LSE; ++i) lv[i] = plse[min(sg + i * RED_SG, ns - 1) * lse_step];
+  const uint32_t st = a.status[wbase + (int64_t)min(tid, ns - 1) * G];
   u32x2 v[RED_PER_WAVE];
 #pragma unroll
-  for (int u = 0; u < RED_PER_WAVE; ++u)
-    v[u] = __builtin_nontemporal_load(&src[min(wave + u * RED_WAVES, ns - 1) * split_step]);   // read once
-  const uint32_t st = a.status[wbase + (int64_t)min(tid, ns - 1) * G];
+  for (int u = 0; u < RED_PER_WAVE; ++u) {
+    const u32x2* ps = src + min(wave + u * RED_WAVES, ns - 1) * split_step;   // uniform
+    v[u] = __builtin_nontemporal_load(ps + lane);   // read once
+  }
 
   // per-row max over the splits
   float m = -INFINITY;
@@ -934,16 +940,19 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   red_w[sg][row] = wsum;
   __syncthreads();
 
-  // weighted sum of this wave's pieces (a split whose coefficient is 0 adds
-  // nothing, whatever its partial holds)
+  // weighted sum of this wave's pieces.  Partials are finite (a row without
+  // visible keys stores zeros), so a split whose coefficient is 0 adds an
+  // exact 0.
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < RED_PER_WAVE; ++u) {
-    const int s = wave + u * RED_WAVES;
-    const float c = s < ns ? coef[s][prow] : 0.f;
-    const f16x4 h = __builtin_bit_cast(f16x4, v[u]);
-    const f32x4 x = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-    if (c != 0.f) acc += c * x;
+    const int s = wave + u * RED_WAVES;   // uniform
+    if (s < ns) {
+      const float c = coef[s][prow];
+      const f16x4 h = __builtin_bit_cast(f16x4, v[u]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(c, (float)h[i], acc[i]);
+    }
   }
   part[wave][lane] = acc;
   __syncthreads();
