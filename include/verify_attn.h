@@ -113,8 +113,10 @@ typedef struct va_plan {
 #define VA_PLAN_VERSION 2u
 
 /* How verify_attn_run decomposes the keys of a request (va_plan.mode).
- * VA_MODE_FUSED: one partial kernel; its splits cover slices of all L + T
- *   keys, and the tiles that reach into the draft block apply the tree mask.
+ * VA_MODE_FUSED: one partial kernel; its nsplit splits cover equal slices
+ *   of the L prefix keys (whole 32-key blocks), the last one followed by the
+ *   T draft keys, and the tiles that reach into the draft block apply the
+ *   tree mask.
  * VA_MODE_SPLIT_TREE: the split-verify decomposition ("The Architecture
  *   Detective", section "The Split Verify Design": the draft queries attend
  *   the prefix densely, only the small tree block needs the custom mask, and
@@ -146,8 +148,10 @@ typedef struct va_plan {
  * The number of KV splits per request (the grid dimension of the partial
  * pass; "The Verify Kernel Breakthrough", section "The Message in Context",
  * raised it from 16 to 64 for occupancy) is chosen from the compute-unit
- * count, the rows T_r*H and the key counts so that every work item gets a
- * similar number of keys.  The environment variable VA_NSPLIT, read here
+ * count, the rows T_r*H and the prefix lengths so that every work item gets
+ * a similar number of prefix keys in whole tiles (the T_r <= 64 draft keys
+ * add at most one tile to the request's last split) and the work items fit
+ * the compute units.  The environment variable VA_NSPLIT, read here
  * only, forces one split count for every request (for tuning sweeps; with
  * VA_PLAN_SPLIT_TREE it is the count of prefix splits).
  * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_HIP (device query failed).

@@ -390,9 +390,11 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   }
   int k0, k1;   // key range of this split (keys past a short table dropped)
   if (MODE == FUSED) {
-    const int chunk = ((n + ns - 1) / ns + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
-    k0 = s * chunk;
-    k1 = min(n_valid, k0 + chunk);
+    // the L prefix keys in ns slices of whole SPLIT_ALIGN blocks; the T
+    // draft keys go with the last slice
+    const int chunk = ((L + ns - 1) / ns + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
+    k0 = min(s * chunk, L);
+    k1 = min(n_valid, s == ns - 1 ? n : min(k0 + chunk, L));
   } else if (MODE == PREFIX) {
     const int np = ns - 1;   // >= 1 here
     const int chunk = ((L + np - 1) / np + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
@@ -1259,21 +1261,24 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   p.num_cus = num_cus;
   p.mode = split_tree ? VA_MODE_SPLIT_TREE : VA_MODE_FUSED;
 
-  // Split count: balance keys x row groups over the compute units (in the
-  // split-tree mode over the prefix keys only; the tree block is one more
-  // split per request, run by its own small kernel).
+  // Split count: balance prefix keys x row groups over the compute units.
+  // The draft keys (at most one tile) go with each request's last split in
+  // the fused mode, and to the tree block, one more split per request run by
+  // its own small kernel, in the split-tree mode.
   int64_t units = 0;
   int64_t cus = num_cus;
   for (int r = 0; r < num_requests; ++r) {
     const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
-    units += groups * ((int64_t)h_prefix_len[r] + (split_tree ? 0 : h_num_tree[r]));
+    units += groups * (int64_t)h_prefix_len[r];
     if (split_tree) cus -= groups;   // compute units the tree-block work items occupy
   }
   if (cus < 1) cus = 1;
   // A work item takes ceil(keys / TILE) tile iterations whatever the keys in
   // its last tile, so the split length is rounded up to whole tiles: the
-  // same iterations on the critical path, fewer splits to write and merge
-  // (the 65k-prefix request: 114 splits of 576 keys instead of 128 of 544).
+  // same iterations on the critical path, fewer splits to write and merge.
+  // (The 65k-prefix request, H = 8, T = 16: 128 splits of 512 prefix keys,
+  // 8 tiles each, the last split 16 draft keys more.  Spreading all L + T
+  // keys instead gave 114 splits of 576 keys, 9 tiles each.)
   auto whole_tiles = [](int64_t k) { return (k + TILE - 1) / TILE * TILE; };
   int64_t keys_per_item = whole_tiles((units + cus - 1) / cus);
   if (keys_per_item < MIN_KEYS_PER_SPLIT) keys_per_item = MIN_KEYS_PER_SPLIT;
@@ -1281,7 +1286,7 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   if (const char* e = std::getenv("VA_NSPLIT")) forced = std::atoi(e);
   // prefix split count of request r for a given split length
   auto nsplit_of = [&](int r, int64_t kpi) -> int64_t {
-    const int64_t n = (int64_t)h_prefix_len[r] + (split_tree ? 0 : h_num_tree[r]);
+    const int64_t n = h_prefix_len[r];
     int64_t ns = forced > 0 ? forced : (n + kpi - 1) / kpi;
     const int64_t max_ns = (n + SPLIT_ALIGN - 1) / SPLIT_ALIGN;
     const int64_t cap = split_tree ? VA_MAX_SPLITS - 1 : VA_MAX_SPLITS;

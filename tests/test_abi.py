@@ -53,16 +53,15 @@ def test_plan_long_prefix_h8_t16():
     p = _plan(8, [65536], [16])
     assert p.magic == binding.VA_PLAN_MAGIC and p.rows_per_group == 64 and p.tile_keys == 64
     assert p.num_groups[0] == 2                     # 128 rows / 64
-    # keys x groups spread over 256 CUs: ceil(2 * 65552 / 256) = 513 keys per
-    # work item, i.e. 9 tile iterations; rounded up to whole tiles (576 keys)
-    # that is ceil(65552 / 576) = 114 splits
-    assert p.nsplit[0] == 114
-    assert p.total_work == 228
+    # prefix keys x groups spread over 256 CUs: 2 * 65536 / 256 = 512 keys (8
+    # tiles) per work item, 128 splits; the 16 draft keys go with the last
+    assert p.nsplit[0] == 128
+    assert p.total_work == 256
     assert p.total_tree == 16 and p.total_rows == 128
-    o = 228 * 64 * 512 * 2                          # fp16 partial outputs
+    o = 256 * 64 * 512 * 2                          # fp16 partial outputs
     assert p.lse_offset == o
-    assert p.status_offset == o + 228 * 64 * 8
-    assert p.workspace_bytes == o + 228 * 64 * 8 + 1024
+    assert p.status_offset == o + 256 * 64 * 8
+    assert p.workspace_bytes == o + 256 * 64 * 8 + 1024
 
 
 def test_plan_full_heads_and_ragged_batch():
@@ -84,9 +83,9 @@ def test_plan_full_heads_and_ragged_batch():
 
 def test_plan_small_inputs_keep_a_minimum_split_length():
     p = _plan(8, [256], [4])
-    assert p.num_groups[0] == 1 and p.nsplit[0] == 3      # 260 keys, >= 128 per split
+    assert p.num_groups[0] == 1 and p.nsplit[0] == 2      # 256 prefix keys, >= 128 per split
     p = _plan(8, [4096], [16])
-    assert p.num_groups[0] == 2 and p.nsplit[0] == 33     # 4112 keys in splits of >= 128
+    assert p.num_groups[0] == 2 and p.nsplit[0] == 32     # 4096 prefix keys in splits of >= 128
     p = _plan(1, [0], [1])
     assert p.nsplit[0] == 1 and p.total_work == 1 and p.total_rows == 1
 

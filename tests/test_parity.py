@@ -150,7 +150,7 @@ def test_edge_shapes(case):
     check(wl, out, lse, what="edge")
 
 
-@pytest.mark.parametrize("nsplit", [1, 2, 3, 7, 64, 129])
+@pytest.mark.parametrize("nsplit", [1, 2, 3, 7, 64, 128])
 def test_split_count_does_not_change_the_result(nsplit, monkeypatch):
     wl = inputs.make_workload("ns", 8, [16], [4096], 16384, seed=3)
     monkeypatch.setenv("VA_NSPLIT", str(nsplit))
