@@ -24,6 +24,10 @@ HIPCC_FLAGS = [
     # as an MFMA operand in AGPRs and its output accumulators in VGPRs; the
     # AGPR-result form makes the allocator copy the accumulators every tile
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # the leading scalar kernel arguments (up to 16 dwords) arrive preloaded
+    # in scalar registers: the partial and merge kernels pass the pointers
+    # their first loads need there, which saves one dependent load at entry
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -306,13 +306,38 @@ struct PartialSmem {
 };
 static_assert(sizeof(PartialSmem::xp) >= VA_MAX_TREE * sizeof(uint64_t), "ancestor masks fit");
 
-template <int MODE>
-__device__ __forceinline__ void partial_body(const PartialArgs& a, int block, PartialSmem& sm);
+// The arguments the prologue's first loads depend on.  The kernels take them
+// as leading scalar parameters, ahead of the argument struct, and the library
+// is built with kernel-argument preloading, so they arrive in scalar
+// registers at wave launch: the request-length and slot-table loads go out
+// without first waiting for a kernel-argument load.  ONE (a plan with a
+// single request) also takes that request's split count, row groups, draft
+// nodes and prefix bound from here instead of the struct's arrays.
+struct Lead {
+  const int32_t* prefix_len;
+  const int32_t* slot_indptr;
+  const int32_t* slot_table;
+  const uint16_t* q;
+  int32_t total_work;
+  int32_t num_heads;
+  int32_t slot_table_len;
+  int32_t ns0, g0, t0, max_prefix0;   // request 0 (used when ONE)
+};
+
+template <int MODE, bool ONE>
+__device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f, int block,
+                                             PartialSmem& sm);
 
 // FUSED launch: one block per work item (XCD-ordered, see partial_body).
-__global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
+template <bool ONE>
+__global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(
+    const int32_t* prefix_len, const int32_t* slot_indptr, const int32_t* slot_table,
+    const uint16_t* q, int32_t total_work, int32_t num_heads, int32_t slot_table_len, int32_t ns0,
+    int32_t g0, int32_t t0, int32_t max_prefix0, PartialArgs a) {
   __shared__ PartialSmem sm;
-  partial_body<FUSED>(a, blockIdx.x, sm);
+  const Lead f{prefix_len, slot_indptr, slot_table, q, total_work, num_heads, slot_table_len,
+               ns0, g0, t0, max_prefix0};
+  partial_body<FUSED, ONE>(a, f, blockIdx.x, sm);
 }
 
 // SPLIT_TREE launch: the tree-block work items (blocks 0 .. tree_blocks-1)
@@ -320,12 +345,15 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(PartialArgs a) {
 // its own compute units alongside the prefix splits instead of before them.
 __global__ __launch_bounds__(THREADS, 1) void va_split_kernel(PartialArgs a, int tree_blocks) {
   __shared__ PartialSmem sm;
-  if ((int)blockIdx.x < tree_blocks) partial_body<TREE>(a, blockIdx.x, sm);
-  else partial_body<PREFIX>(a, blockIdx.x - tree_blocks, sm);
+  const Lead f{a.prefix_len, a.slot_indptr, a.slot_table, a.q, a.total_work, a.num_heads,
+               a.slot_table_len, 0, 0, 0, 0};
+  if ((int)blockIdx.x < tree_blocks) partial_body<TREE, false>(a, f, blockIdx.x, sm);
+  else partial_body<PREFIX, false>(a, f, blockIdx.x - tree_blocks, sm);
 }
 
-template <int MODE>
-__device__ __forceinline__ void partial_body(const PartialArgs& a, int block, PartialSmem& sm) {
+template <int MODE, bool ONE>
+__device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f, int block,
+                                             PartialSmem& sm) {
   uint16_t* const tiles = sm.tiles;
   bf16x8 (&xp)[2][2][2][64] = sm.xp;
   int32_t (&sring)[SLOT_RING][TILE] = sm.sring;
@@ -356,37 +384,39 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     if (b >= a.num_groups[r]) return;
     w = a.work_begin[r] + (a.nsplit[r] - 1) * a.num_groups[r] + b;
   } else {
-    const int per_xcd = (a.total_work + 7) >> 3;
+    const int per_xcd = (f.total_work + 7) >> 3;
     w = (block & 7) * per_xcd + (block >> 3);
-    if (w >= a.total_work) return;
-    while (r + 1 < a.num_requests && a.work_begin[r + 1] <= w) ++r;
+    if (w >= f.total_work) return;
+    if (!ONE) while (r + 1 < a.num_requests && a.work_begin[r + 1] <= w) ++r;
   }
-  const int G = a.num_groups[r];
-  const int local = w - a.work_begin[r];
+  const int G = ONE ? f.g0 : a.num_groups[r];
+  const int local = w - (ONE ? 0 : a.work_begin[r]);
   const int s = local / G;
   const int g = local - s * G;
-  const int ns = a.nsplit[r];
+  const int ns = ONE ? f.ns0 : a.nsplit[r];
   if (MODE == PREFIX && s == ns - 1) return;   // the tree block
-  const int T = a.num_tree[r];
-  const int H = a.num_heads;
+  const int T = ONE ? f.t0 : a.num_tree[r];
+  const int H = f.num_heads;
+  const int tb = ONE ? 0 : a.tree_begin[r];
   const int rows_r = T * H;
 
   if (tid == 0) status_sh = 0u;
 
   uint32_t st = 0u;
-  int L = a.prefix_len[r];
-  if (L < 0 || L > a.max_prefix[r]) {
+  const int maxp = ONE ? f.max_prefix0 : a.max_prefix[r];
+  int L = f.prefix_len[r];
+  if (L < 0 || L > maxp) {
     st |= VA_STATUS_BAD_PREFIX;
-    L = L < 0 ? 0 : a.max_prefix[r];
+    L = L < 0 ? 0 : maxp;
   }
   const int n = L + T;
-  const int tab0 = a.slot_indptr[r];
-  const int tab1 = a.slot_indptr[r + 1];
+  const int tab0 = f.slot_indptr[r];
+  const int tab1 = f.slot_indptr[r + 1];
   int n_valid = n;   // keys whose table entry exists
-  if (tab0 < 0 || tab1 < tab0 || tab1 > a.slot_table_len || tab1 - tab0 < n) {
+  if (tab0 < 0 || tab1 < tab0 || tab1 > f.slot_table_len || tab1 - tab0 < n) {
     st |= VA_STATUS_SHORT_TABLE;
-    n_valid = (tab0 < 0 || tab1 < tab0 || tab0 >= a.slot_table_len)
-                  ? 0 : min(min(tab1, a.slot_table_len) - tab0, n);
+    n_valid = (tab0 < 0 || tab1 < tab0 || tab0 >= f.slot_table_len)
+                  ? 0 : min(min(tab1, f.slot_table_len) - tab0, n);
   }
   int k0, k1;   // key range of this split (keys past a short table dropped)
   if (MODE == FUSED) {
@@ -405,7 +435,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
     k1 = min(n_valid, n);
   }
   const int ntiles = k1 > k0 ? (k1 - k0 + TILE - 1) / TILE : 0;
-  const int32_t* table = a.slot_table + (n_valid > 0 ? tab0 : 0);
+  const int32_t* table = f.slot_table + (n_valid > 0 ? tab0 : 0);
 
   // ---- slot-table entries of the first two tiles: the first copies wait on
   // them, so they go out before everything else.  Wave 0 copies the 64
@@ -425,7 +455,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   // last row (free until the first tile is consumed); lanes past T re-read
   // entry T-1
   if (MODE != PREFIX && wave == 0)
-    dma4_v(lds_addr(&sring[SLOT_RING - 1][0]), a.parent + a.tree_begin[r] + min(lane, T - 1));
+    dma4_v(lds_addr(&sring[SLOT_RING - 1][0]), a.parent + tb + min(lane, T - 1));
 
   // ---- Q, all 576 score columns of the group's rows
   const int rho = g * ROWS + rh * 32 + lrow;
@@ -441,7 +471,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, int block, Pa
   // the second tile's copies start after the barrier at the top of the
   // first tile, when every wave has read its fragments.
   {
-    const uint16_t* const q0 = a.q + (int64_t)a.tree_begin[r] * H * DQK;
+    const uint16_t* const q0 = f.q + (int64_t)tb * H * DQK;
     const uint16_t* src[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -868,9 +898,15 @@ constexpr int RED_WAVES = RED_THREADS / 64;
 constexpr int RED_SG = RED_THREADS / 32;    // split groups of the lse loads
 constexpr int RED_PIECES = 2 * O_BLK * 4;   // blocks per row group
 
-// MAXS: a bound on every request's split count, a multiple of RED_SG
-template <int MAXS>
-__global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
+// MAXS: a bound on every request's split count, a multiple of RED_SG.
+// The pointers and, when ONE (a single request), that request's split count,
+// row groups and rows come as leading scalar parameters, preloaded into
+// scalar registers like the partial kernel's (see Lead), so the first loads
+// need no kernel-argument load.
+template <int MAXS, bool ONE>
+__global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(
+    const uint32_t* part_o, const float* part_lse, const uint32_t* status, uint16_t* out,
+    float* lse, int32_t ns0, int32_t g0, int32_t rows0, int32_t num_heads, ReduceArgs a) {
   constexpr int RED_LSE = MAXS / RED_SG;           // lse pairs per thread
   constexpr int RED_PER_WAVE = MAXS / RED_WAVES;   // pieces per lane
   __shared__ float coef[MAXS][32];
@@ -886,34 +922,37 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
   int b = blockIdx.x;
   int r = 0;
   // block ranges: request r owns num_groups[r] * RED_PIECES blocks
-  while (r + 1 < a.num_requests && b >= a.num_groups[r] * RED_PIECES) {
-    b -= a.num_groups[r] * RED_PIECES;
-    ++r;
+  if (!ONE) {
+    while (r + 1 < a.num_requests && b >= a.num_groups[r] * RED_PIECES) {
+      b -= a.num_groups[r] * RED_PIECES;
+      ++r;
+    }
   }
   const int g = b / RED_PIECES;
   const int piece = b - g * RED_PIECES;    // (rh * 16 + cb) * 4 + qd
   const int rh = piece / (O_BLK * 4);
   const int cb = (piece >> 2) % O_BLK;
   const int qd = piece & 3;
-  const int ns = a.nsplit[r];
-  const int G = a.num_groups[r];
-  const int H = a.num_heads;
-  const int rows_r = (a.tree_begin[r + 1] - a.tree_begin[r]) * H;
-  const int64_t wbase = (int64_t)a.work_begin[r] + g;   // work item of split s: wbase + s * G
+  const int ns = ONE ? ns0 : a.nsplit[r];
+  const int G = ONE ? g0 : a.num_groups[r];
+  const int H = num_heads;
+  const int rows_r = ONE ? rows0 : (a.tree_begin[r + 1] - a.tree_begin[r]) * H;
+  const int tb = ONE ? 0 : a.tree_begin[r];
+  const int64_t wbase = (int64_t)(ONE ? 0 : a.work_begin[r]) + g;   // work item of split s: wbase + s * G
 
   const int row = tid & 31;
   const int sg = tid >> 5;   // 2 wave + lane / 32
   const int prow = lane & 31;
   // lse pair of split s: plse[s * lse_step] (s * lse_step < 2^31: at most
   // 256 splits of at most 1024 row groups of 64 rows)
-  const float2* plse = reinterpret_cast<const float2*>(a.part_lse) + wbase * ROWS + rh * 32 + row;
+  const float2* plse = reinterpret_cast<const float2*>(part_lse) + wbase * ROWS + rh * 32 + row;
   const int lse_step = G * ROWS;
-  const u32x2* src = reinterpret_cast<const u32x2*>(a.part_o) + wbase * PART_VEC + piece * 64;
+  const u32x2* src = reinterpret_cast<const u32x2*>(part_o) + wbase * PART_VEC + piece * 64;
   const int64_t split_step = (int64_t)G * PART_VEC;
   float2 lv[RED_LSE];
 #pragma unroll
   for (int i = 0; i < RED_LSE; ++i) lv[i] = plse[min(sg + i * RED_SG, ns - 1) * lse_step];
-  const uint32_t st = a.status[wbase + (int64_t)min(tid, ns - 1) * G];
+  const uint32_t st = status[wbase + (int64_t)min(tid, ns - 1) * G];
   u32x2 v[RED_PER_WAVE];
 #pragma unroll
   for (int u = 0; u < RED_PER_WAVE; ++u) {
@@ -985,12 +1024,12 @@ __global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(ReduceArgs a) {
         res[0] = res[1] = res[2] = res[3] = 0.f;
         lse_out = -INFINITY;
       }
-      const int64_t orow = (int64_t)a.tree_begin[r] * H + rr;
+      const int64_t orow = (int64_t)tb * H + rr;
       const int col = cb * 32 + 8 * qd + 4 * (lane >> 5);
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[0]) | ((uint32_t)f32_to_bf16_rne(res[1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[2]) | ((uint32_t)f32_to_bf16_rne(res[3]) << 16);
-      *reinterpret_cast<uint2*>(a.out + orow * DV + col) = make_uint2(lo, hi);
-      if ((piece & (O_BLK * 4 - 1)) == 0 && lane < 32) a.lse[orow] = lse_out;   // once per row
+      *reinterpret_cast<uint2*>(out + orow * DV + col) = make_uint2(lo, hi);
+      if ((piece & (O_BLK * 4 - 1)) == 0 && lane < 32) lse[orow] = lse_out;   // once per row
     }
   }
 }
@@ -1155,7 +1194,17 @@ int launch_partial(const va_plan* plan, const uint16_t* q, const uint16_t* kv_po
     hipLaunchKernelGGL(va_split_kernel, dim3(grid + (unsigned)tree_blocks), dim3(THREADS), 0, st,
                        a, tree_blocks);
   } else {
-    hipLaunchKernelGGL(va_partial_kernel, dim3(grid), dim3(THREADS), 0, st, a);
+    const bool one = plan->num_requests == 1;
+    const int ns0 = plan->nsplit[0], g0 = plan->num_groups[0], t0 = plan->num_tree[0];
+    const int mp0 = plan->max_prefix[0];
+    if (one)
+      hipLaunchKernelGGL(va_partial_kernel<true>, dim3(grid), dim3(THREADS), 0, st, prefix_len,
+                         slot_indptr, slot_table, q, a.total_work, a.num_heads, slot_table_len, ns0,
+                         g0, t0, mp0, a);
+    else
+      hipLaunchKernelGGL(va_partial_kernel<false>, dim3(grid), dim3(THREADS), 0, st, prefix_len,
+                         slot_indptr, slot_table, q, a.total_work, a.num_heads, slot_table_len, ns0,
+                         g0, t0, mp0, a);
   }
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
@@ -1185,16 +1234,22 @@ int launch_reduce(const va_plan* plan, const char* ws, uint16_t* out, float* lse
     blocks += plan->num_groups[r] * RED_PIECES;
     max_ns = max(max_ns, plan->nsplit[r]);
   }
-  if (max_ns <= 16)
-    hipLaunchKernelGGL(va_reduce_kernel<16>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else if (max_ns <= 32)
-    hipLaunchKernelGGL(va_reduce_kernel<32>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else if (max_ns <= 64)
-    hipLaunchKernelGGL(va_reduce_kernel<64>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else if (max_ns <= 128)
-    hipLaunchKernelGGL(va_reduce_kernel<128>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(va_reduce_kernel<VA_MAX_SPLITS>, dim3(blocks), dim3(RED_THREADS), 0, st, a);
+  const bool one = plan->num_requests == 1;
+  const int ns0 = plan->nsplit[0], g0 = plan->num_groups[0];
+  const int rows0 = plan->num_tree[0] * plan->num_heads;
+  auto launch = [&](auto k1, auto k0) {
+    if (one)
+      hipLaunchKernelGGL(k1, dim3(blocks), dim3(RED_THREADS), 0, st, a.part_o, a.part_lse,
+                         a.status, out, lse, ns0, g0, rows0, a.num_heads, a);
+    else
+      hipLaunchKernelGGL(k0, dim3(blocks), dim3(RED_THREADS), 0, st, a.part_o, a.part_lse,
+                         a.status, out, lse, ns0, g0, rows0, a.num_heads, a);
+  };
+  if (max_ns <= 16) launch(va_reduce_kernel<16, true>, va_reduce_kernel<16, false>);
+  else if (max_ns <= 32) launch(va_reduce_kernel<32, true>, va_reduce_kernel<32, false>);
+  else if (max_ns <= 64) launch(va_reduce_kernel<64, true>, va_reduce_kernel<64, false>);
+  else if (max_ns <= 128) launch(va_reduce_kernel<128, true>, va_reduce_kernel<128, false>);
+  else launch(va_reduce_kernel<VA_MAX_SPLITS, true>, va_reduce_kernel<VA_MAX_SPLITS, false>);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
