@@ -312,7 +312,10 @@ static_assert(sizeof(PartialSmem::xp) >= VA_MAX_TREE * sizeof(uint64_t), "ancest
 // registers at wave launch: the request-length and slot-table loads go out
 // without first waiting for a kernel-argument load.  ONE (a plan with a
 // single request) also takes that request's split count, row groups, draft
-// nodes and prefix bound from here instead of the struct's arrays.
+// nodes and prefix bound from here instead of the struct's arrays.  14
+// dwords are preloaded (16 user SGPRs less the argument-segment pointer):
+// the parameters are ordered so that only the last ones, needed after the
+// first loads return, come from memory.
 struct Lead {
   const int32_t* prefix_len;
   const int32_t* slot_indptr;
@@ -343,12 +346,16 @@ __global__ __launch_bounds__(THREADS, 1) void va_partial_kernel(
 // SPLIT_TREE launch: the tree-block work items (blocks 0 .. tree_blocks-1)
 // and the prefix work items share one grid, so the small tree block runs on
 // its own compute units alongside the prefix splits instead of before them.
-__global__ __launch_bounds__(THREADS, 1) void va_split_kernel(PartialArgs a, int tree_blocks) {
+template <bool ONE>
+__global__ __launch_bounds__(THREADS, 1) void va_split_kernel(
+    const int32_t* prefix_len, const int32_t* slot_indptr, const int32_t* slot_table,
+    const uint16_t* q, int32_t tree_blocks, int32_t total_work, int32_t num_heads,
+    int32_t slot_table_len, int32_t ns0, int32_t g0, int32_t t0, int32_t max_prefix0, PartialArgs a) {
   __shared__ PartialSmem sm;
-  const Lead f{a.prefix_len, a.slot_indptr, a.slot_table, a.q, a.total_work, a.num_heads,
-               a.slot_table_len, 0, 0, 0, 0};
-  if ((int)blockIdx.x < tree_blocks) partial_body<TREE, false>(a, f, blockIdx.x, sm);
-  else partial_body<PREFIX, false>(a, f, blockIdx.x - tree_blocks, sm);
+  const Lead f{prefix_len, slot_indptr, slot_table, q, total_work, num_heads, slot_table_len,
+               ns0, g0, t0, max_prefix0};
+  if ((int)blockIdx.x < tree_blocks) partial_body<TREE, ONE>(a, f, blockIdx.x, sm);
+  else partial_body<PREFIX, ONE>(a, f, blockIdx.x - tree_blocks, sm);
 }
 
 template <int MODE, bool ONE>
@@ -377,12 +384,17 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
   if (MODE == TREE) {
     // block b -> (request, row group) of the tree-block work items
     int b = block;
-    while (r + 1 < a.num_requests && b >= a.num_groups[r]) {
-      b -= a.num_groups[r];
-      ++r;
+    if (ONE) {
+      if (b >= f.g0) return;
+      w = (f.ns0 - 1) * f.g0 + b;
+    } else {
+      while (r + 1 < a.num_requests && b >= a.num_groups[r]) {
+        b -= a.num_groups[r];
+        ++r;
+      }
+      if (b >= a.num_groups[r]) return;
+      w = a.work_begin[r] + (a.nsplit[r] - 1) * a.num_groups[r] + b;
     }
-    if (b >= a.num_groups[r]) return;
-    w = a.work_begin[r] + (a.nsplit[r] - 1) * a.num_groups[r] + b;
   } else {
     const int per_xcd = (f.total_work + 7) >> 3;
     w = (block & 7) * per_xcd + (block >> 3);
@@ -1188,16 +1200,22 @@ int launch_partial(const va_plan* plan, const uint16_t* q, const uint16_t* kv_po
     a.work_begin[r] = plan->work_begin[r];
   }
   const unsigned grid = 8u * (unsigned)((plan->total_work + 7) / 8);   // see the XCD work order
+  // request 0's values for the single-request instantiations (see Lead)
+  const int ns0 = plan->nsplit[0], g0 = plan->num_groups[0], t0 = plan->num_tree[0];
+  const int mp0 = plan->max_prefix[0];
   if (plan->mode == VA_MODE_SPLIT_TREE) {
     int tree_blocks = 0;
     for (int r = 0; r < plan->num_requests; ++r) tree_blocks += plan->num_groups[r];
-    hipLaunchKernelGGL(va_split_kernel, dim3(grid + (unsigned)tree_blocks), dim3(THREADS), 0, st,
-                       a, tree_blocks);
+    if (plan->num_requests == 1)
+      hipLaunchKernelGGL(va_split_kernel<true>, dim3(grid + (unsigned)tree_blocks), dim3(THREADS), 0,
+                         st, prefix_len, slot_indptr, slot_table, q, tree_blocks, a.total_work,
+                         a.num_heads, slot_table_len, ns0, g0, t0, mp0, a);
+    else
+      hipLaunchKernelGGL(va_split_kernel<false>, dim3(grid + (unsigned)tree_blocks), dim3(THREADS),
+                         0, st, prefix_len, slot_indptr, slot_table, q, tree_blocks, a.total_work,
+                         a.num_heads, slot_table_len, ns0, g0, t0, mp0, a);
   } else {
-    const bool one = plan->num_requests == 1;
-    const int ns0 = plan->nsplit[0], g0 = plan->num_groups[0], t0 = plan->num_tree[0];
-    const int mp0 = plan->max_prefix[0];
-    if (one)
+    if (plan->num_requests == 1)
       hipLaunchKernelGGL(va_partial_kernel<true>, dim3(grid), dim3(THREADS), 0, st, prefix_len,
                          slot_indptr, slot_table, q, a.total_work, a.num_heads, slot_table_len, ns0,
                          g0, t0, mp0, a);
