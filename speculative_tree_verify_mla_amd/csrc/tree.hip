@@ -28,14 +28,10 @@
 
 namespace {
 
+// The rest of the arguments (the inputs come as leading scalar parameters).
 struct TreeArgs {
-  const int32_t* raw_parent;   // [sum T_r]
-  const int32_t* raw_slot;     // [sum T_r]
-  const int32_t* prefix_len;   // [B]
-  const int32_t* slot_indptr;  // [B+1]
   int32_t* slot_table;
   int32_t slot_table_len;
-  int32_t num_requests;
   int32_t* perm;               // [sum T_r]
   int32_t* parent;             // [sum T_r]
   uint64_t* anc;               // [sum T_r]
@@ -43,12 +39,21 @@ struct TreeArgs {
   int32_t tree_begin[VA_MAX_REQUESTS + 1];
 };
 
-__global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
+// The inputs of the first loads come as leading scalar parameters, which the
+// library's build preloads into scalar registers (no kernel-argument load
+// before them); ONE (a single request) also takes its node count from there.
+template <bool ONE>
+__global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* raw_parent,
+                                                        const int32_t* raw_slot,
+                                                        const int32_t* prefix_len,
+                                                        const int32_t* slot_indptr,
+                                                        int32_t num_requests, int32_t t_first,
+                                                        TreeArgs a) {
   const int r = blockIdx.x;
-  if (r >= a.num_requests) return;
+  if (r >= num_requests) return;
   const int lane = threadIdx.x;
-  const int t0 = a.tree_begin[r];
-  const int T = a.tree_begin[r + 1] - t0;
+  const int t0 = ONE ? 0 : a.tree_begin[r];
+  const int T = ONE ? t_first : a.tree_begin[r + 1] - t0;
   const bool live = lane < T;
   uint32_t bad = 0u;
 
@@ -58,11 +63,11 @@ __global__ __launch_bounds__(64) void build_tree_kernel(TreeArgs a) {
   // walk still going after 64 steps (more than T) is a cycle.
   // every load up front: the walk, the ranking and the table write then need
   // no further round trip to memory
-  int p = live ? a.raw_parent[t0 + lane] : -1;
-  const int32_t my_slot = live ? a.raw_slot[t0 + lane] : 0;
-  const int32_t tab_base = a.slot_indptr[r];
-  const int64_t tab_lo = (int64_t)tab_base + a.prefix_len[r];
-  const int32_t tab_hi = a.slot_indptr[r + 1];
+  int p = live ? raw_parent[t0 + lane] : -1;
+  const int32_t my_slot = live ? raw_slot[t0 + lane] : 0;
+  const int32_t tab_base = slot_indptr[r];
+  const int64_t tab_lo = (int64_t)tab_base + prefix_len[r];
+  const int32_t tab_hi = slot_indptr[r + 1];
   if (live && (p < -1 || p >= T)) {
     bad = VA_TREE_BAD_PARENT;
     p = -1;
@@ -141,20 +146,21 @@ int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const
       return VA_ERR_PLAN;
   if (slot_table_len < 0) return VA_ERR_SHAPE;
   TreeArgs a;
-  a.raw_parent = raw_parent;
-  a.raw_slot = raw_slot;
-  a.prefix_len = prefix_len;
-  a.slot_indptr = slot_indptr;
   a.slot_table = slot_table;
   a.slot_table_len = slot_table_len;
-  a.num_requests = plan->num_requests;
   a.perm = perm;
   a.parent = parent;
   a.anc = anc;
   a.status = status;
   for (int r = 0; r <= plan->num_requests; ++r) a.tree_begin[r] = plan->tree_begin[r];
-  hipLaunchKernelGGL(build_tree_kernel, dim3(plan->num_requests), dim3(64), 0,
-                     static_cast<hipStream_t>(stream), a);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan->num_requests == 1)
+    hipLaunchKernelGGL(build_tree_kernel<true>, dim3(1), dim3(64), 0, st, raw_parent, raw_slot,
+                       prefix_len, slot_indptr, plan->num_requests, plan->num_tree[0], a);
+  else
+    hipLaunchKernelGGL(build_tree_kernel<false>, dim3(plan->num_requests), dim3(64), 0, st,
+                       raw_parent, raw_slot, prefix_len, slot_indptr, plan->num_requests,
+                       plan->num_tree[0], a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
