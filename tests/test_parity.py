@@ -449,3 +449,34 @@ def test_device_data_errors_poison_only_their_request():
     assert status & 1
     assert torch.isnan(o[8:].float()).all()
     assert torch.equal(o[:8].view(torch.int16), good_o[:8].view(torch.int16))
+
+
+def test_single_request_table_offset_and_device_errors():
+    """A single request (the launches that take its values as preloaded
+    kernel arguments): its table slice may start anywhere in the slot table,
+    and a device prefix above the planned bound or a short slice still poison
+    the rows and set the status bits."""
+    wl = inputs.make_workload("one", 8, [16], [700], 4096, seed=41, table="interleaved")
+    good_o, good_l, status, plan = run_gpu(wl)
+    assert status == 0
+    check(wl, good_o, good_l, what="offset 0")
+    # the same slots behind 37 unrelated entries
+    junk = np.arange(37, dtype=np.int32) % wl.num_slots
+    off = inputs.Workload(**{**wl.__dict__, "slot_table": np.concatenate([junk, wl.slot_table]),
+                             "slot_indptr": (wl.slot_indptr + 37).astype(np.int32)})
+    o, l, status, _ = run_gpu(off, plan=plan)
+    assert status == 0
+    assert torch.equal(o.view(torch.int16), good_o.view(torch.int16))
+    assert torch.equal(l.view(torch.int32), good_l.view(torch.int32))
+    # device prefix above the planned bound
+    d = Dev(wl)
+    d.prefix.fill_(701)
+    o, l, status, _ = run_gpu(wl, d=d, plan=plan)
+    assert status & 1
+    assert torch.isnan(o.float()).all() and torch.isnan(l).all()
+    # a slice shorter than L + T
+    short = inputs.Workload(**{**wl.__dict__,
+                               "slot_indptr": np.array([0, 700 + 16 - 3], np.int32)})
+    o, l, status, _ = run_gpu(short, plan=plan)
+    assert status & 2
+    assert torch.isnan(o.float()).all() and torch.isnan(l).all()
