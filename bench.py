@@ -203,6 +203,16 @@ def measure_marshal(torch, va, inputs, dev, time_graph):
         pre, ind, tab = t(wl.prefix_len), t(wl.slot_indptr), t(wl.slot_table)
         ms = time_graph(lambda i: va.verify_attn_build_tree(plan, rp, rs, pre, ind, tab), 200)
         res[f"us_{name}"] = round(ms * 1e3, 3)
+        # with the queries gathered into verify order by the library as well
+        q_raw = torch.zeros((int(plan.total_tree), 8, 576), dtype=torch.bfloat16, device=dev)
+        q_v = torch.empty_like(q_raw)
+
+        def marshal_q(i):
+            perm = va.verify_attn_build_tree(plan, rp, rs, pre, ind, tab)[0]
+            va.verify_attn_permute_rows(plan, perm, q_raw, q_v)
+
+        ms = time_graph(marshal_q, 200)
+        res[f"us_{name}_with_q"] = round(ms * 1e3, 3)
     res["pages_host_tree_and_mask_ms"] = 1.98
     return res
 

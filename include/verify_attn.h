@@ -365,7 +365,8 @@ int verify_attn_compact(uint16_t* kv_pool, int64_t num_slots, int32_t kv_row_str
  *                perm[i] is the raw node at position i, parent[i] its
  *                parent's position or -1 - ready for verify_attn_run.
  * anc            [sum T_r] uint64 out: bit k set iff position k is i or an
- *                ancestor of i (the tree mask, as the kernel uses it).
+ *                ancestor of i (the tree mask; verify_attn_run builds the
+ *                same masks itself from `parent`, so it needs no anc input).
  * status         [B] uint32 out: 0, or VA_TREE_* bits for a request whose
  *                raw tree is not a forest or whose draft entries do not all
  *                fall inside its table range (a short range or a negative
@@ -381,6 +382,27 @@ int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const
                            const int32_t* prefix_len, const int32_t* slot_indptr,
                            int32_t* slot_table, int32_t slot_table_len, int32_t* perm,
                            int32_t* parent, uint64_t* anc, uint32_t* status, va_stream_t stream);
+
+/*
+ * verify_attn_permute_rows - gather per-node rows from raw node order into
+ * verify order (enqueue only): the step between verify_attn_build_tree and
+ * verify_attn_run for queries produced in raw node order, so that raw trees
+ * in, verify outputs out is a sequence of library calls on one stream.
+ *
+ * perm       [sum T_r] device: from verify_attn_build_tree (request-local raw
+ *            node of each verify position).
+ * src        [sum T_r, row_elems] bf16 device: one row per raw node, requests
+ *            concatenated as in `plan` (for q: row_elems = H * 576).
+ * dst        [sum T_r, row_elems] bf16 device out:
+ *            dst[t0 + i] = src[t0 + perm[t0 + i]] for request r starting at
+ *            t0 = tree_begin[r].  A perm entry outside [0, T_r) (a request
+ *            verify_attn_build_tree flagged) gives a row of zeros.
+ * row_elems  elements per row, >= 8 and a multiple of 8 (16-byte pieces).
+ * src and dst are 16-byte aligned and must not overlap.
+ * Errors (host): VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_SHAPE, VA_ERR_ALIGN, VA_ERR_HIP.
+ */
+int verify_attn_permute_rows(const va_plan* plan, const int32_t* perm, const uint16_t* src,
+                             uint16_t* dst, int64_t row_elems, va_stream_t stream);
 
 #ifdef __cplusplus
 }

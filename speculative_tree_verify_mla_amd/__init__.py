@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     verify_attn_error_string,
     verify_attn_forward_static,
     verify_attn_gather_rows,
+    verify_attn_permute_rows,
     verify_attn_stream_read,
     verify_attn_plan,
     verify_attn_read_status,

@@ -42,7 +42,7 @@ EXPORTS = (
     "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_stream_read",
     "verify_attn_error_string",
     "verify_attn_plan_struct_size", "verify_attn_compact_workspace_bytes", "verify_attn_compact",
-    "verify_attn_build_tree",
+    "verify_attn_build_tree", "verify_attn_permute_rows",
 )
 TREE_BITS = {1: "BAD_PARENT", 2: "BAD_TABLE"}
 COMPACT_BITS = {1: "BAD_SLOT", 2: "RUN_OCCUPIED"}
@@ -113,6 +113,8 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_compact.restype = ctypes.c_int
     lib.verify_attn_build_tree.argtypes = [ctypes.POINTER(VaPlan), P, P, P, P, P, i32, P, P, P, P, P]
     lib.verify_attn_build_tree.restype = ctypes.c_int
+    lib.verify_attn_permute_rows.argtypes = [ctypes.POINTER(VaPlan), P, P, P, i64, P]
+    lib.verify_attn_permute_rows.restype = ctypes.c_int
     lib.verify_attn_plan_struct_size.argtypes = []
     lib.verify_attn_plan_struct_size.restype = sz
     for name in ("verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
@@ -352,6 +354,27 @@ def verify_attn_build_tree(plan, raw_parent, raw_slot, prefix_len, slot_indptr, 
         _dptr(anc, (torch.int64,), "anc"), _dptr(status, i32, "status"), _stream_handle(stream))
     _check("verify_attn_build_tree", rc)
     return perm, parent, anc, status
+
+
+def verify_attn_permute_rows(plan, perm, src, dst=None, stream=None):
+    """Enqueue the gather of per-node rows from raw node order into verify
+    order (dst[t0 + i] = src[t0 + perm[t0 + i]] per request).  src: [sum T_r,
+    ...] bf16 (for q: [sum T_r, H, 576]); dst: same shape (allocated if None).
+    Returns dst."""
+    import torch
+    n = int(plan.total_tree)
+    if src.shape[0] != n or perm.numel() != n:
+        raise ValueError("src and perm need sum(T_r) rows")
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst.shape != src.shape:
+        raise ValueError("dst must have the shape of src")
+    b16 = _bf16_types()
+    rc = load_library().verify_attn_permute_rows(
+        ctypes.byref(plan), _dptr(perm, (torch.int32,), "perm"), _dptr(src, b16, "src"),
+        _dptr(dst, b16, "dst"), int(src.numel() // n), _stream_handle(stream))
+    _check("verify_attn_permute_rows", rc)
+    return dst
 
 
 # --------------------------------------------------------------------------- convenience

@@ -19,6 +19,9 @@
 // One wave per request, lane j = raw node j.  A parent outside [-1, T_r) or
 // a cycle sets the request's status bit (VA_TREE_BAD_PARENT); its outputs are
 // then unspecified, and nothing is written outside the request's own ranges.
+//
+// permute_rows_kernel then gathers per-node rows (the queries, H x 576 bf16
+// per node) from raw order into verify order through perm.
 
 #include <hip/hip_runtime.h>
 
@@ -27,6 +30,8 @@
 #include "verify_attn.h"
 
 namespace {
+
+typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
 
 // The rest of the arguments (the inputs come as leading scalar parameters).
 struct TreeArgs {
@@ -122,6 +127,36 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* raw_paren
   if (lane == 0) a.status[r] = bits;
 }
 
+// dst row t0 + i = src row t0 + perm[t0 + i]: block (x, R) copies 16-byte
+// pieces 256 x .. 256 x + 255 of verify row R.  Pointers and sizes come as
+// leading (preloaded) arguments; ONE (a single request) needs no table.
+struct PermuteArgs {
+  int32_t num_requests;
+  int32_t tree_begin[VA_MAX_REQUESTS + 1];
+};
+constexpr int PERMUTE_THREADS = 256;
+
+template <bool ONE>
+__global__ __launch_bounds__(PERMUTE_THREADS) void permute_rows_kernel(
+    const int32_t* perm, const vec4u* src, vec4u* dst, int64_t pieces, int32_t t_first,
+    PermuteArgs a) {
+  const int R = blockIdx.y;
+  const int64_t p = (int64_t)blockIdx.x * PERMUTE_THREADS + threadIdx.x;
+  if (p >= pieces) return;
+  int t0 = 0, T = t_first;
+  if (!ONE) {
+    int r = 0;
+    while (r + 1 < a.num_requests && a.tree_begin[r + 1] <= R) ++r;
+    t0 = a.tree_begin[r];
+    T = a.tree_begin[r + 1] - t0;
+  }
+  const int j = perm[R];
+  vec4u v = {0u, 0u, 0u, 0u};
+  // each source row is read once
+  if (j >= 0 && j < T) v = __builtin_nontemporal_load(src + (int64_t)(t0 + j) * pieces + p);
+  dst[(int64_t)R * pieces + p] = v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,6 +196,39 @@ int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const
     hipLaunchKernelGGL(build_tree_kernel<false>, dim3(plan->num_requests), dim3(64), 0, st,
                        raw_parent, raw_slot, prefix_len, slot_indptr, plan->num_requests,
                        plan->num_tree[0], a);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+int verify_attn_permute_rows(const va_plan* plan, const int32_t* perm, const uint16_t* src,
+                             uint16_t* dst, int64_t row_elems, va_stream_t stream) {
+  if (plan == nullptr || perm == nullptr || src == nullptr || dst == nullptr) return VA_ERR_NULL;
+  if (plan->magic != VA_PLAN_MAGIC || plan->version != VA_PLAN_VERSION ||
+      plan->num_requests < 1 || plan->num_requests > VA_MAX_REQUESTS || plan->tree_begin[0] != 0 ||
+      plan->total_tree != plan->tree_begin[plan->num_requests] || plan->total_tree < 1)
+    return VA_ERR_PLAN;
+  for (int r = 0; r < plan->num_requests; ++r)
+    if (plan->num_tree[r] < 1 || plan->num_tree[r] > VA_MAX_TREE ||
+        plan->tree_begin[r + 1] - plan->tree_begin[r] != plan->num_tree[r])
+      return VA_ERR_PLAN;
+  if (row_elems < 8 || (row_elems % 8) != 0 || row_elems > ((int64_t)1 << 40)) return VA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15u) != 0)
+    return VA_ERR_ALIGN;
+  const int64_t pieces = row_elems / 8;
+  const int64_t xblocks = (pieces + PERMUTE_THREADS - 1) / PERMUTE_THREADS;
+  if (xblocks > INT32_MAX) return VA_ERR_SHAPE;
+  PermuteArgs a;
+  a.num_requests = plan->num_requests;
+  for (int r = 0; r <= plan->num_requests; ++r) a.tree_begin[r] = plan->tree_begin[r];
+  const dim3 grid((unsigned)xblocks, (unsigned)plan->total_tree);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const vec4u* s4 = reinterpret_cast<const vec4u*>(src);
+  vec4u* d4 = reinterpret_cast<vec4u*>(dst);
+  if (plan->num_requests == 1)
+    hipLaunchKernelGGL(permute_rows_kernel<true>, grid, dim3(PERMUTE_THREADS), 0, st, perm, s4, d4,
+                       pieces, plan->num_tree[0], a);
+  else
+    hipLaunchKernelGGL(permute_rows_kernel<false>, grid, dim3(PERMUTE_THREADS), 0, st, perm, s4,
+                       d4, pieces, plan->num_tree[0], a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 

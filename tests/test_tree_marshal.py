@@ -117,8 +117,9 @@ def test_negative_device_prefix_writes_only_its_own_table_range():
 
 
 def test_marshal_then_verify_in_one_graph():
-    """Raw trees in, verify outputs out, all captured in one HIP graph; rows
-    come out in verify order and match the oracle on the marshaled inputs."""
+    """Raw trees in, verify outputs out, all captured in one HIP graph of
+    library calls (marshal, query permutation, verify); rows come out in
+    verify order and match the oracle on the marshaled inputs."""
     wl, rp, rs, q_raw = _raw_batch([16, 9], [700, 1200], seed=21)
     d = Dev(wl)
     table = wl.slot_table.copy()
@@ -134,7 +135,6 @@ def test_marshal_then_verify_in_one_graph():
     H = wl.num_heads
     out = torch.empty((25, H, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((25, H), dtype=torch.float32, device=DEV)
-    base = torch.tensor([0] * 16 + [16] * 9, dtype=torch.int64, device=DEV)   # request offsets
     torch.cuda.synchronize()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -143,7 +143,7 @@ def test_marshal_then_verify_in_one_graph():
         with torch.cuda.graph(g, stream=st):
             perm, parent, anc, status = va.verify_attn_build_tree(
                 plan, raw_p, raw_s, d.prefix, d.indptr, d.table, stream=st)
-            qv.copy_(qr.index_select(0, perm.long() + base))
+            va.verify_attn_permute_rows(plan, perm, qr, qv, stream=st)
             va.verify_attn(qv, d.kv, d.table, d.indptr, d.prefix, parent, wl.sm_scale,
                            num_tree=wl.num_tree, prefix_len_host=wl.prefix_len, plan=plan,
                            workspace=ws, out=out, lse=lse, stream=st)
@@ -158,3 +158,30 @@ def test_marshal_then_verify_in_one_graph():
     q_v = np.concatenate([q_raw[:16][perm_h[:16]], q_raw[16:][perm_h[16:]]])
     wl_v = inputs.Workload(**{**wl.__dict__, "q": q_v, "parent": ref[1], "slot_table": ref[4]})
     check(wl_v, out, lse, what="marshal+verify graph")
+
+
+def test_permute_rows_gathers_through_perm():
+    """verify_attn_permute_rows against a host gather, bit for bit, for one and
+    several requests; a perm entry outside the request's nodes gives zeros."""
+    for num_tree in ([16], [3, 64, 1, 17]):
+        H = 8
+        plan = va.verify_attn_plan(H, [100] * len(num_tree), num_tree)
+        n = int(plan.total_tree)
+        rng = np.random.default_rng(len(num_tree))
+        perm = np.concatenate([rng.permutation(t) for t in num_tree]).astype(np.int32)
+        perm[1 if len(num_tree) == 1 else 5] = 70                  # outside [0, T_r)
+        src = rng.standard_normal((n, H, 576)).astype(np.float32)
+        src_b = torch.from_numpy(inputs.bf16_bits(src).view(np.int16)).to(DEV).view(torch.bfloat16)
+        dst = va.verify_attn_permute_rows(plan, torch.from_numpy(perm).to(DEV), src_b)
+        torch.cuda.synchronize()
+        got = dst.view(torch.int16).cpu().numpy()
+        want = np.zeros_like(got)
+        srch = src_b.view(torch.int16).cpu().numpy()
+        t0 = 0
+        for t in num_tree:
+            for i in range(t):
+                j = int(perm[t0 + i])
+                if 0 <= j < t:
+                    want[t0 + i] = srch[t0 + j]
+            t0 += t
+        np.testing.assert_array_equal(got, want)
