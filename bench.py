@@ -217,6 +217,52 @@ def measure_marshal(torch, va, inputs, dev, time_graph):
     return res
 
 
+def measure_restart(torch, va, inputs, wl, pool, table, indptr, prefix, parent, H, stream,
+                    time_graph, us_plain_warm):
+    """The fixed-reference softmax's slow path at the bench shape.  The rope
+    columns of tile j (0..7) of every 512-key split get j*c added, with q =
+    0.5 + 0.1 N(0, 1) so that every row's score climbs by about 24 log2 units
+    per 64-key tile.  Tile 3 of each split then beats the split's first-tile
+    reference by more than the 64-unit slack: every work item stops its first
+    pass, sweeps its split for the exact row maxima, and computes the split
+    again, the three-pass worst case.  One pool copy (warm), against the warm
+    plain call."""
+    import math
+    dev = pool.device
+    T = int(wl.num_tree.sum())
+    L = int(wl.prefix_len[0])
+    rng = np.random.default_rng(5)
+    q_r = torch.from_numpy(inputs.bf16_bits(
+        (0.5 + 0.1 * rng.standard_normal((T, H, 576))).astype(np.float32)).view(np.int16)).to(dev)
+    q_r = q_r.view(torch.bfloat16)
+    step_log2 = 24.0
+    c = step_log2 / (0.5 * 64 * wl.sm_scale / math.log(2.0))
+    rows = table[:L].long()
+    k = torch.arange(L, device=dev)
+    bump = (c * ((k // 64) % 8).float()).unsqueeze(1)
+    pool_r = pool.clone()
+    pool_r[rows, 512:] = (pool_r[rows, 512:].float() + bump).to(torch.bfloat16)
+    plan = va.verify_attn_plan(H, wl.prefix_len, wl.num_tree)
+    ws = va.workspace_for(plan, dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def step(i):
+        va.verify_attn_run(plan, q_r, pool_r, table, indptr, prefix, parent, wl.sm_scale, ws, stream)
+        va.verify_attn_reduce(plan, ws, out, lse, stream)
+
+    with torch.cuda.stream(stream):
+        step(0)
+    torch.cuda.synchronize()
+    status = va.verify_attn_read_status(plan, ws, stream)
+    finite = bool(torch.isfinite(out.float()).all() and torch.isfinite(lse).all())
+    ms = time_graph(step, 50)
+    return {"workload": "the bench shape, scores rising ~24 log2 units per tile within every split",
+            "passes": 3, "us_per_call": round(ms * 1e3, 3),
+            "vs_plain_warm": round(ms * 1e3 / us_plain_warm, 3),
+            "status": int(status), "finite": finite}
+
+
 def measure_config(torch, va, inputs, dev, stream, idx, n_pools, steps):
     """One of the other workloads (full head count, ragged batch): µs per call
     from a HIP graph of `steps` calls rotating over `n_pools` pool copies,
@@ -464,6 +510,11 @@ def main():
 
     marshal = measure_marshal(torch, va, inputs, dev, capture_timer(torch, stream))
 
+    restart = None
+    if args.workload == WORKLOAD:
+        restart = measure_restart(torch, va, inputs, wl, pools[0], table, indptr, prefix, parent,
+                                  H, stream, capture_timer(torch, stream), ms_warm * 1e3)
+
     other = None
     if not args.no_other_configs:
         # the MFMA-bound workloads: all 64 heads over a 200k prefix, and the
@@ -583,6 +634,7 @@ def main():
         "other_configs": other,
         "defrag": defrag,
         "tree_marshal": marshal,
+        "restart_path": restart,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "wall_s_timed": round(t_wall, 3),
