@@ -270,9 +270,10 @@ int verify_attn_read_status(const va_plan* plan, const void* workspace, va_strea
 int verify_attn_check_tree(const int32_t* h_parent, int32_t T);
 
 /*
- * verify_attn_gather_rows - diagnostic copy of pool rows through the same
- * 16-byte gather path the partial pass uses: dst[k, 0:576] =
- * kv_pool[slot_table[k], 0:576] for k < n.  dst is [n, 576] bf16, 16-byte
+ * verify_attn_gather_rows - diagnostic copy of pool rows through the partial
+ * pass's own tile loader (its slot-table ring, 16-byte copy sources and copy
+ * instructions into its LDS tile layout, 64 keys per tile), read back out of
+ * LDS: dst[k, 0:576] = kv_pool[slot_table[k], 0:576] for k < n.  dst is [n, 576] bf16, 16-byte
  * aligned.  Slots outside [0, num_slots) yield rows of NaN.  Enqueue only.
  * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_ALIGN, VA_ERR_HIP.
  */

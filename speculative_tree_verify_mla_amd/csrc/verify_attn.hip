@@ -280,6 +280,25 @@ __device__ __forceinline__ constexpr int piece_off(int k, int p) {
   return (p >> 3) * LINE + (k >> 3) * CHUNK + (k & 7) * 128 + (((p & 7) ^ swz(k)) << 4);
 }
 
+// The tile loader's lane roles.  Wave w copies the 9 lines of tile keys
+// 16w .. 16w+15 (18 copies of 1 KB: 8 keys x 128 bytes); lane l takes key
+// tile_key(w, e, l) (e = 0, 1), whose slot it reads from the slot ring, and
+// the 16-byte piece (l % 8) ^ swz(key) of each of that key's lines.
+__device__ __forceinline__ int tile_key(int wave, int e, int lane) {
+  return 16 * wave + 8 * e + (lane >> 3);
+}
+// Global source of the lane's piece of line 0 of tile key `key`: the slot's
+// pool row, or the zero row for a key past the split end (exists false) or a
+// slot outside the pool (which also sets VA_STATUS_BAD_SLOT in bad).  The
+// copy of line J then reads 128 J bytes further.
+__device__ __forceinline__ const uint16_t* copy_source(const uint16_t* kv, int64_t num_slots,
+                                                       int32_t stride, int32_t slot, bool exists,
+                                                       int key, int lane, uint32_t& bad) {
+  const bool inside = slot >= 0 && (int64_t)slot < num_slots;
+  if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
+  return (exists && inside ? kv + (int64_t)slot * stride : va_zero_row) + 8 * ((lane & 7) ^ swz(key));
+}
+
 // Which keys a launch of the partial kernel covers.
 //   FUSED:  every split of a request covers a slice of its L + T keys; tiles
 //           reaching into the draft block apply the tree mask.
@@ -513,7 +532,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
   auto read_slots = [&](int u) -> SlotPair {
     SlotPair sp;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) sp.v[e] = sring[u & (SLOT_RING - 1)][16 * wave + 8 * e + (lane >> 3)];
+    for (int e = 0; e < 2; ++e) sp.v[e] = sring[u & (SLOT_RING - 1)][tile_key(wave, e, lane)];
     return sp;
   };
   // vslot: read_slots(u), read ahead by the caller
@@ -521,13 +540,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
     TileIssue ti;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int key = 16 * wave + 8 * e + (lane >> 3);
-      const int k = k0 + u * TILE + key;
-      const bool exists = k < k1;
-      const bool inside = vslot.v[e] >= 0 && (int64_t)vslot.v[e] < a.num_slots;
-      if (exists && !inside) bad = VA_STATUS_BAD_SLOT;
-      ti.src[e] = (exists && inside ? a.kv + (int64_t)vslot.v[e] * a.stride : va_zero_row) +
-                  8 * ((lane & 7) ^ swz(key));
+      const int key = tile_key(wave, e, lane);
+      ti.src[e] = copy_source(a.kv, a.num_slots, a.stride, vslot.v[e], k0 + u * TILE + key < k1,
+                              key, lane, bad);
     }
     ti.lds_w = lds_addr(buf) + 2 * wave * CHUNK;
     return ti;
@@ -1079,25 +1094,49 @@ __global__ __launch_bounds__(STREAM_THREADS) void va_stream_read_kernel(const u3
   }
 }
 
-// Diagnostic: pool rows through the partial pass's table/slot checks and its
-// 16-byte global->LDS copy; one block of 64 threads per row.
-__global__ __launch_bounds__(64) void va_gather_kernel(const uint16_t* kv, int64_t num_slots,
-                                                       int32_t stride, const int32_t* table,
-                                                       int32_t n, uint16_t* dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t row_lds[DQK];
-  const int k = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int32_t slot = table_entry(table, k, n);
-  const bool inside = slot >= 0 && (int64_t)slot < num_slots;
-  const uint16_t* row = inside ? kv + (int64_t)slot * stride : va_zero_row;
-  dma16(row + lane * 8, row_lds);                        // latent pieces 0..63
-  if (lane < NPIECE - 64) dma16(row + DV + lane * 8, row_lds + DV);   // rope pieces 64..71
+// Diagnostic: pool rows through the partial kernel's own tile loader, one
+// block per 64-key tile: its slot-ring copy of the table entries, its lane
+// roles and copy sources (tile_key, copy_source), its copy instructions
+// (dma_part) and its LDS tile layout (piece_off), then the rows read back out
+// of the tile in table order.
+__global__ __launch_bounds__(THREADS) void va_gather_kernel(const uint16_t* kv, int64_t num_slots,
+                                                            int32_t stride, const int32_t* table,
+                                                            int32_t n, uint16_t* dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[BUF_ELEMS];
+  __shared__ int32_t ring[TILE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k0 = blockIdx.x * TILE;
+  const int k1 = min(n, k0 + TILE);
+  // the slot entries of the tile, as the partial kernel's slot ring gets them
+  if (wave == 0) dma4_v(lds_addr(ring), table + min(k0 + lane, k1 - 1));
   wait_vmcnt<0>();
   __syncthreads();
-  for (int i = lane; i < DQK / 8; i += 64) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(row_lds + i * 8);
-    if (!inside) v = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-    *reinterpret_cast<u32x4*>(dst + (int64_t)k * DQK + i * 8) = v;
+  // the partial kernel's copies of one tile: its lane roles, sources and
+  // copy instructions, into its LDS layout
+  uint32_t bad = 0u;
+  const uint16_t* src[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int key = tile_key(wave, e, lane);
+    src[e] = copy_source(kv, num_slots, stride, ring[key], k0 + key < k1, key, lane, bad);
+  }
+  const uint32_t lds_w = lds_addr(tile) + 2 * wave * CHUNK;
+#pragma unroll
+  for (int part = 0; part < COPIES / 2; ++part)
+    dma_part(part, lds_w, src[0], src[1], std::make_integer_sequence<int, COPIES / 2>{});
+  vm_wait<0>();
+  __syncthreads();
+  // rows back out of the tile layout (NaN rows for slots outside the pool)
+  for (int i = tid; i < TILE * NPIECE; i += THREADS) {
+    const int key = i / NPIECE;
+    const int p = i - key * NPIECE;
+    if (k0 + key >= k1) continue;
+    const int32_t slot = ring[key];
+    u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(tile) + piece_off(key, p));
+    if (slot < 0 || (int64_t)slot >= num_slots) v = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+    *reinterpret_cast<u32x4*>(dst + (int64_t)(k0 + key) * DQK + p * 8) = v;
   }
 }
 
@@ -1503,7 +1542,7 @@ int verify_attn_gather_rows(const uint16_t* kv_pool, int64_t num_slots, int32_t 
   if (n < 0 || num_slots < 1 || kv_row_stride < DQK) return VA_ERR_SHAPE;
   if (!aligned16(kv_pool) || !aligned16(dst) || (kv_row_stride % 8) != 0) return VA_ERR_ALIGN;
   if (n == 0) return VA_OK;
-  hipLaunchKernelGGL(va_gather_kernel, dim3((unsigned)n), dim3(64), 0,
+  hipLaunchKernelGGL(va_gather_kernel, dim3((unsigned)((n + TILE - 1) / TILE)), dim3(THREADS), 0,
                      static_cast<hipStream_t>(stream), kv_pool, num_slots, kv_row_stride,
                      slot_table, n, dst);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
