@@ -341,6 +341,9 @@ def parse():
                     help="skip the 2 GiB streaming-read calibration")
     ap.add_argument("--no-defrag", action="store_true",
                     help="skip the compaction (Tier 1 defrag) measurement")
+    ap.add_argument("--no-restart", action="store_true",
+                    help="skip the softmax slow-path leg (profiling runs: its three-pass launches "
+                         "would mix into the partial kernel's per-dispatch counter means)")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the full-head and ragged-batch workloads")
     ap.add_argument("--workload", type=int, default=WORKLOAD,
@@ -511,7 +514,7 @@ def main():
     marshal = measure_marshal(torch, va, inputs, dev, capture_timer(torch, stream))
 
     restart = None
-    if args.workload == WORKLOAD:
+    if args.workload == WORKLOAD and not args.no_restart:
         restart = measure_restart(torch, va, inputs, wl, pools[0], table, indptr, prefix, parent,
                                   H, stream, capture_timer(torch, stream), ms_warm * 1e3)
 
