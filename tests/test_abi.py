@@ -297,3 +297,22 @@ def test_build_tree_refuses_tampered_plans_before_launch(field, value):
     f = _fake
     assert lib.verify_attn_build_tree(ctypes.byref(bad), f(4096), f(4096), f(4096), f(4096),
                                       f(4096), 100, f(4096), f(4096), f(4096), f(4096), None) == -5
+    assert lib.verify_attn_permute_rows(ctypes.byref(bad), f(4096), f(4096), f(8192), 4608,
+                                        None) == -5
+
+
+def test_permute_rows_argument_errors_before_launch():
+    """verify_attn_permute_rows checks its arguments on the host; every case
+    here returns before a launch (so no GPU)."""
+    lib = va.load_library()
+    plan = _plan(8, [100, 50], [4, 6])
+    f = _fake
+    p = ctypes.byref(plan)
+    assert lib.verify_attn_permute_rows(None, f(4096), f(4096), f(8192), 4608, None) == -1
+    assert lib.verify_attn_permute_rows(p, None, f(4096), f(8192), 4608, None) == -1
+    assert lib.verify_attn_permute_rows(p, f(4096), None, f(8192), 4608, None) == -1
+    assert lib.verify_attn_permute_rows(p, f(4096), f(4096), None, 4608, None) == -1
+    assert lib.verify_attn_permute_rows(p, f(4096), f(4096), f(8192), 4607, None) == -2   # not x8
+    assert lib.verify_attn_permute_rows(p, f(4096), f(4096), f(8192), 0, None) == -2
+    assert lib.verify_attn_permute_rows(p, f(4096), f(4104), f(8192), 4608, None) == -3   # src
+    assert lib.verify_attn_permute_rows(p, f(4096), f(4096), f(8200), 4608, None) == -3   # dst
