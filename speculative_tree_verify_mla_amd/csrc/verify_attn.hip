@@ -909,31 +909,36 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
   if (tid == 0) a.status[w] = status_sh;
 }
 
-// Log-sum-exp merge of the splits.  One block of 512 threads per (request,
-// row group, row half, 32-column block, 4-column quad):
-// 32 rows x 8 columns, read as one contiguous 512-byte piece per split.
+// Log-sum-exp merge of the splits.  One block per (request, row group, row
+// half, 32-column block, 4-column quad): 32 rows x 8 columns, read as one
+// contiguous 512-byte piece per split.  The block has 256 threads for up to
+// 64 splits and 512 beyond (red_threads): with few splits the shorter
+// barriers of four waves pay, with many the eight waves' loads in flight.
 // All of the block's loads go out together, so the merge costs one memory
 // round trip: thread (split group sg, row) loads the (lse, scale exponent e)
-// pairs of splits sg, sg + 16, ..., wave v the pieces of splits v, v + 8,
-// ..., and thread i the status word of split i.  Loads past the request's
+// pairs of splits sg, sg + SG, ... (SG = threads / 32), wave v the pieces of
+// splits v, v + W, ... (W = threads / 64), and thread i the status word of
+// split i.  Loads past the request's
 // last split re-read that split (in bounds, no branch around any load) and
 // are dropped.  Then, on registers and LDS: the row max over the splits, the
 // coefficients exp2(lse_s - max) * 2^e_s, each wave's weighted sum of its
 // pieces, and the sum over the waves.
-constexpr int RED_THREADS = 512;
-constexpr int RED_WAVES = RED_THREADS / 64;
-constexpr int RED_SG = RED_THREADS / 32;    // split groups of the lse loads
 constexpr int RED_PIECES = 2 * O_BLK * 4;   // blocks per row group
+constexpr int red_threads(int maxs) { return maxs <= 64 ? 256 : 512; }
 
-// MAXS: a bound on every request's split count, a multiple of RED_SG.
+// MAXS: a bound on every request's split count, a multiple of the split
+// groups (red_threads(MAXS) / 32).
 // The pointers and, when ONE (a single request), that request's split count,
 // row groups and rows come as leading scalar parameters, preloaded into
 // scalar registers like the partial kernel's (see Lead), so the first loads
 // need no kernel-argument load.
 template <int MAXS, bool ONE>
-__global__ __launch_bounds__(RED_THREADS) void va_reduce_kernel(
+__global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
     const uint32_t* part_o, const float* part_lse, const uint32_t* status, uint16_t* out,
     float* lse, int32_t ns0, int32_t g0, int32_t rows0, int32_t num_heads, ReduceArgs a) {
+  constexpr int RED_WAVES = red_threads(MAXS) / 64;
+  constexpr int RED_SG = red_threads(MAXS) / 32;    // split groups of the lse loads
+  static_assert(MAXS % RED_SG == 0 && MAXS % RED_WAVES == 0, "split bound");
   constexpr int RED_LSE = MAXS / RED_SG;           // lse pairs per thread
   constexpr int RED_PER_WAVE = MAXS / RED_WAVES;   // pieces per lane
   __shared__ float coef[MAXS][32];
@@ -1294,19 +1299,21 @@ int launch_reduce(const va_plan* plan, const char* ws, uint16_t* out, float* lse
   const bool one = plan->num_requests == 1;
   const int ns0 = plan->nsplit[0], g0 = plan->num_groups[0];
   const int rows0 = plan->num_tree[0] * plan->num_heads;
-  auto launch = [&](auto k1, auto k0) {
+  auto launch = [&](auto k1, auto k0, int threads) {
     if (one)
-      hipLaunchKernelGGL(k1, dim3(blocks), dim3(RED_THREADS), 0, st, a.part_o, a.part_lse,
+      hipLaunchKernelGGL(k1, dim3(blocks), dim3(threads), 0, st, a.part_o, a.part_lse,
                          a.status, out, lse, ns0, g0, rows0, a.num_heads, a);
     else
-      hipLaunchKernelGGL(k0, dim3(blocks), dim3(RED_THREADS), 0, st, a.part_o, a.part_lse,
+      hipLaunchKernelGGL(k0, dim3(blocks), dim3(threads), 0, st, a.part_o, a.part_lse,
                          a.status, out, lse, ns0, g0, rows0, a.num_heads, a);
   };
-  if (max_ns <= 16) launch(va_reduce_kernel<16, true>, va_reduce_kernel<16, false>);
-  else if (max_ns <= 32) launch(va_reduce_kernel<32, true>, va_reduce_kernel<32, false>);
-  else if (max_ns <= 64) launch(va_reduce_kernel<64, true>, va_reduce_kernel<64, false>);
-  else if (max_ns <= 128) launch(va_reduce_kernel<128, true>, va_reduce_kernel<128, false>);
-  else launch(va_reduce_kernel<VA_MAX_SPLITS, true>, va_reduce_kernel<VA_MAX_SPLITS, false>);
+#define VA_RED(M) launch(va_reduce_kernel<M, true>, va_reduce_kernel<M, false>, red_threads(M))
+  if (max_ns <= 16) VA_RED(16);
+  else if (max_ns <= 32) VA_RED(32);
+  else if (max_ns <= 64) VA_RED(64);
+  else if (max_ns <= 128) VA_RED(128);
+  else VA_RED(VA_MAX_SPLITS);
+#undef VA_RED
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
