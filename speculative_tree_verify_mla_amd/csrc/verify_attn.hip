@@ -911,7 +911,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
 
 // Log-sum-exp merge of the splits.  One block per (request, row group, row
 // half, 32-column block, 4-column quad): 32 rows x 8 columns, read as one
-// contiguous 512-byte piece per split.  The block has 256 threads for up to
+// contiguous 512-byte piece per split; with QPB = 4, all four quads of the
+// 32-column block (four consecutive pieces, wave q finishing quad q).  The block has 256 threads for up to
 // 64 splits and 512 beyond (red_threads): with few splits the shorter
 // barriers of four waves pay, with many the eight waves' loads in flight.
 // All of the block's loads go out together, so the merge costs one memory
@@ -932,7 +933,7 @@ constexpr int red_threads(int maxs) { return maxs <= 64 ? 256 : 512; }
 // row groups and rows come as leading scalar parameters, preloaded into
 // scalar registers like the partial kernel's (see Lead), so the first loads
 // need no kernel-argument load.
-template <int MAXS, bool ONE>
+template <int MAXS, int QPB, bool ONE>
 __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
     const uint32_t* part_o, const float* part_lse, const uint32_t* status, uint16_t* out,
     float* lse, int32_t ns0, int32_t g0, int32_t rows0, int32_t num_heads, ReduceArgs a) {
@@ -940,11 +941,13 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
   constexpr int RED_SG = red_threads(MAXS) / 32;    // split groups of the lse loads
   static_assert(MAXS % RED_SG == 0 && MAXS % RED_WAVES == 0, "split bound");
   constexpr int RED_LSE = MAXS / RED_SG;           // lse pairs per thread
-  constexpr int RED_PER_WAVE = MAXS / RED_WAVES;   // pieces per lane
+  constexpr int RED_PER_WAVE = MAXS / RED_WAVES;   // splits per wave
+  constexpr int BPG = RED_PIECES / QPB;            // blocks per row group
+  static_assert(QPB == 1 || (QPB == 4 && RED_WAVES >= 4), "quads per block");
   __shared__ float coef[MAXS][32];
   __shared__ float red_m[RED_SG][32];
   __shared__ float red_w[RED_SG][32];
-  __shared__ f32x4 part[RED_WAVES][64];
+  __shared__ f32x4 part[RED_WAVES][QPB][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -953,15 +956,15 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int b = blockIdx.x;
   int r = 0;
-  // block ranges: request r owns num_groups[r] * RED_PIECES blocks
+  // block ranges: request r owns num_groups[r] * BPG blocks
   if (!ONE) {
-    while (r + 1 < a.num_requests && b >= a.num_groups[r] * RED_PIECES) {
-      b -= a.num_groups[r] * RED_PIECES;
+    while (r + 1 < a.num_requests && b >= a.num_groups[r] * BPG) {
+      b -= a.num_groups[r] * BPG;
       ++r;
     }
   }
-  const int g = b / RED_PIECES;
-  const int piece = b - g * RED_PIECES;    // (rh * 16 + cb) * 4 + qd
+  const int g = b / BPG;
+  const int piece = (b - g * BPG) * QPB;   // first piece: (rh * 16 + cb) * 4 + qd
   const int rh = piece / (O_BLK * 4);
   const int cb = (piece >> 2) % O_BLK;
   const int qd = piece & 3;
@@ -985,11 +988,12 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
 #pragma unroll
   for (int i = 0; i < RED_LSE; ++i) lv[i] = plse[min(sg + i * RED_SG, ns - 1) * lse_step];
   const uint32_t st = status[wbase + (int64_t)min(tid, ns - 1) * G];
-  u32x2 v[RED_PER_WAVE];
+  u32x2 v[RED_PER_WAVE][QPB];
 #pragma unroll
   for (int u = 0; u < RED_PER_WAVE; ++u) {
     const u32x2* ps = src + min(wave + u * RED_WAVES, ns - 1) * split_step;   // uniform
-    v[u] = __builtin_nontemporal_load(ps + lane);   // read once
+#pragma unroll
+    for (int q = 0; q < QPB; ++q) v[u][q] = __builtin_nontemporal_load(ps + q * 64 + lane);   // read once
   }
 
   // per-row max over the splits
@@ -1016,23 +1020,31 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
   // weighted sum of this wave's pieces.  Partials are finite (a row without
   // visible keys stores zeros), so a split whose coefficient is 0 adds an
   // exact 0.
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[QPB];
+#pragma unroll
+  for (int q = 0; q < QPB; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < RED_PER_WAVE; ++u) {
     const int s = wave + u * RED_WAVES;   // uniform
     if (s < ns) {
       const float c = coef[s][prow];
-      const f16x4 h = __builtin_bit_cast(f16x4, v[u]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(c, (float)h[i], acc[i]);
+      for (int q = 0; q < QPB; ++q) {
+        const f16x4 h = __builtin_bit_cast(f16x4, v[u][q]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[q][i] = __builtin_fmaf(c, (float)h[i], acc[q][i]);
+      }
     }
   }
-  part[wave][lane] = acc;
-  __syncthreads();
-  if (tid < 64) {
-    f32x4 tot = part[0][lane];
 #pragma unroll
-    for (int i = 1; i < RED_WAVES; ++i) tot += part[i][lane];
+  for (int q = 0; q < QPB; ++q) part[wave][q][lane] = acc[q];
+  __syncthreads();
+  // wave q < QPB finishes quad qd + q
+  if (wave < QPB) {
+    const int qq = QPB == 1 ? 0 : wave;
+    f32x4 tot = part[0][qq][lane];
+#pragma unroll
+    for (int i = 1; i < RED_WAVES; ++i) tot += part[i][qq][lane];
     float W = 0.f;
     const uint32_t Sr = any_bad ? 1u : 0u;
     float Mr = red_m[0][prow];
@@ -1057,11 +1069,11 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
         lse_out = -INFINITY;
       }
       const int64_t orow = (int64_t)tb * H + rr;
-      const int col = cb * 32 + 8 * qd + 4 * (lane >> 5);
+      const int col = cb * 32 + 8 * (qd + qq) + 4 * (lane >> 5);
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[0]) | ((uint32_t)f32_to_bf16_rne(res[1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[2]) | ((uint32_t)f32_to_bf16_rne(res[3]) << 16);
       *reinterpret_cast<uint2*>(out + orow * DV + col) = make_uint2(lo, hi);
-      if ((piece & (O_BLK * 4 - 1)) == 0 && lane < 32) lse[orow] = lse_out;   // once per row
+      if (((piece + qq) & (O_BLK * 4 - 1)) == 0 && lane < 32) lse[orow] = lse_out;   // once per row
     }
   }
 }
@@ -1290,16 +1302,22 @@ int launch_reduce(const va_plan* plan, const char* ws, uint16_t* out, float* lse
     a.tree_begin[r] = plan->tree_begin[r];
     a.work_begin[r] = plan->work_begin[r];
   }
-  int blocks = 0;
+  int groups = 0;
   int max_ns = 1;
   for (int r = 0; r < plan->num_requests; ++r) {
-    blocks += plan->num_groups[r] * RED_PIECES;
+    groups += plan->num_groups[r];
     max_ns = max(max_ns, plan->nsplit[r]);
   }
+  // With few splits and more one-quad blocks than one round of the CUs
+  // holds (eight four-wave blocks each), a block takes all four quads of a
+  // 32-column block: one round of blocks instead of several.  The output is
+  // the same bit for bit (same splits per wave, same summation order).
+  const bool wide = max_ns <= 32 && groups * RED_PIECES > 8 * plan->num_cus;
   const bool one = plan->num_requests == 1;
   const int ns0 = plan->nsplit[0], g0 = plan->num_groups[0];
   const int rows0 = plan->num_tree[0] * plan->num_heads;
-  auto launch = [&](auto k1, auto k0, int threads) {
+  auto launch = [&](auto k1, auto k0, int threads, int qpb) {
+    const int blocks = groups * (RED_PIECES / qpb);
     if (one)
       hipLaunchKernelGGL(k1, dim3(blocks), dim3(threads), 0, st, a.part_o, a.part_lse,
                          a.status, out, lse, ns0, g0, rows0, a.num_heads, a);
@@ -1307,13 +1325,17 @@ int launch_reduce(const va_plan* plan, const char* ws, uint16_t* out, float* lse
       hipLaunchKernelGGL(k0, dim3(blocks), dim3(threads), 0, st, a.part_o, a.part_lse,
                          a.status, out, lse, ns0, g0, rows0, a.num_heads, a);
   };
-#define VA_RED(M) launch(va_reduce_kernel<M, true>, va_reduce_kernel<M, false>, red_threads(M))
-  if (max_ns <= 16) VA_RED(16);
+#define VA_RED(M) launch(va_reduce_kernel<M, 1, true>, va_reduce_kernel<M, 1, false>, red_threads(M), 1)
+#define VA_RED4(M) launch(va_reduce_kernel<M, 4, true>, va_reduce_kernel<M, 4, false>, red_threads(M), 4)
+  if (max_ns <= 16 && wide) VA_RED4(16);
+  else if (max_ns <= 16) VA_RED(16);
+  else if (max_ns <= 32 && wide) VA_RED4(32);
   else if (max_ns <= 32) VA_RED(32);
   else if (max_ns <= 64) VA_RED(64);
   else if (max_ns <= 128) VA_RED(128);
   else VA_RED(VA_MAX_SPLITS);
 #undef VA_RED
+#undef VA_RED4
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
