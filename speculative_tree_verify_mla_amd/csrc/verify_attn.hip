@@ -912,18 +912,18 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
 // Log-sum-exp merge of the splits.  One block per (request, row group, row
 // half, 32-column block, 4-column quad): 32 rows x 8 columns, read as one
 // contiguous 512-byte piece per split; with QPB = 4, all four quads of the
-// 32-column block (four consecutive pieces, wave q finishing quad q).  The block has 256 threads for up to
-// 64 splits and 512 beyond (red_threads): with few splits the shorter
-// barriers of four waves pay, with many the eight waves' loads in flight.
-// All of the block's loads go out together, so the merge costs one memory
-// round trip: thread (split group sg, row) loads the (lse, scale exponent e)
-// pairs of splits sg, sg + SG, ... (SG = threads / 32), wave v the pieces of
-// splits v, v + W, ... (W = threads / 64), and thread i the status word of
-// split i.  Loads past the request's
-// last split re-read that split (in bounds, no branch around any load) and
-// are dropped.  Then, on registers and LDS: the row max over the splits, the
-// coefficients exp2(lse_s - max) * 2^e_s, each wave's weighted sum of its
-// pieces, and the sum over the waves.
+// 32-column block (four consecutive pieces, wave q finishing quad q).  The
+// block has 256 threads for up to 64 splits and 512 beyond (red_threads):
+// with few splits the shorter barriers of four waves pay, with many the
+// eight waves' loads in flight.  All of the block's loads go out together,
+// so the merge costs one memory round trip: thread (split group sg, row)
+// loads the (lse, scale exponent e) pairs of splits sg, sg + SG, ...
+// (SG = threads / 32), wave v the pieces of splits v, v + W, ...
+// (W = threads / 64), and thread i the status word of split i.  Loads past
+// the request's last split re-read that split (in bounds, no branch around
+// any load) and are dropped.  Then, on registers and LDS: the row max over
+// the splits, the coefficients exp2(lse_s - max) * 2^e_s, each wave's
+// weighted sum of its pieces, and the sum over the waves.
 constexpr int RED_PIECES = 2 * O_BLK * 4;   // blocks per row group
 constexpr int red_threads(int maxs) { return maxs <= 64 ? 256 : 512; }
 
