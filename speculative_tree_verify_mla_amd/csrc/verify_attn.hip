@@ -948,6 +948,7 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
   __shared__ float red_m[RED_SG][32];
   __shared__ float red_w[RED_SG][32];
   __shared__ f32x4 part[RED_WAVES][QPB][64];
+  __shared__ uint32_t bad_w[RED_WAVES];   // per wave: a split status it loaded is nonzero
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -989,11 +990,18 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
   for (int i = 0; i < RED_LSE; ++i) lv[i] = plse[min(sg + i * RED_SG, ns - 1) * lse_step];
   const uint32_t st = status[wbase + (int64_t)min(tid, ns - 1) * G];
   u32x2 v[RED_PER_WAVE][QPB];
+  {
+    // uniform addresses: split wave + u W by steps of W splits, the request's
+    // last split once past it
+    const u32x2* const last = src + (ns - 1) * split_step;
+    const u32x2* ps = src + wave * split_step;
 #pragma unroll
-  for (int u = 0; u < RED_PER_WAVE; ++u) {
-    const u32x2* ps = src + min(wave + u * RED_WAVES, ns - 1) * split_step;   // uniform
+    for (int u = 0; u < RED_PER_WAVE; ++u) {
+      const u32x2* const pu = wave + u * RED_WAVES < ns ? ps : last;
 #pragma unroll
-    for (int q = 0; q < QPB; ++q) v[u][q] = __builtin_nontemporal_load(ps + q * 64 + lane);   // read once
+      for (int q = 0; q < QPB; ++q) v[u][q] = __builtin_nontemporal_load(pu + q * 64 + lane);   // read once
+      ps += RED_WAVES * split_step;
+    }
   }
 
   // per-row max over the splits
@@ -1001,39 +1009,42 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
 #pragma unroll
   for (int i = 0; i < RED_LSE; ++i) m = sg + i * RED_SG < ns ? fmaxf(m, lv[i].x) : m;
   red_m[sg][row] = m;
-  const int any_bad = __syncthreads_or(st != 0u);
+  // the status words: one flag per wave, read by the finishing waves after
+  // the barriers below (a block-wide reduction would cost barriers of its own)
+  const bool wave_bad = __builtin_amdgcn_ballot_w64(st != 0u) != 0ull;
+  if (lane == 0) bad_w[wave] = wave_bad ? 1u : 0u;
+  __syncthreads();
   float M = red_m[0][row];
 #pragma unroll
   for (int i = 1; i < RED_SG; ++i) M = fmaxf(M, red_m[i][row]);
-  // coefficients and weight sums
+  // coefficients and weight sums, without branches: splits past the
+  // request's last (s < MAXS, so inside the table) get coefficient 0
   float wsum = 0.f;
 #pragma unroll
   for (int i = 0; i < RED_LSE; ++i) {
     const int s = sg + i * RED_SG;
-    const float e = (s >= ns || lv[i].x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(lv[i].x - M);
+    const bool on = s < ns && lv[i].x != -INFINITY && M != -INFINITY;
+    const float e = exp2f(on ? lv[i].x - M : -INFINITY);
     wsum += e;
-    if (s < ns) coef[s][row] = e > 0.f ? ldexpf(e, (int)lv[i].y) : 0.f;
+    coef[s][row] = e > 0.f ? ldexpf(e, (int)lv[i].y) : 0.f;
   }
   red_w[sg][row] = wsum;
   __syncthreads();
 
   // weighted sum of this wave's pieces.  Partials are finite (a row without
-  // visible keys stores zeros), so a split whose coefficient is 0 adds an
-  // exact 0.
+  // visible keys stores zeros), so a split whose coefficient is 0, including
+  // the re-read copies of the last split, adds an exact 0.
   f32x4 acc[QPB];
 #pragma unroll
   for (int q = 0; q < QPB; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < RED_PER_WAVE; ++u) {
-    const int s = wave + u * RED_WAVES;   // uniform
-    if (s < ns) {
-      const float c = coef[s][prow];
+    const float c = coef[wave + u * RED_WAVES][prow];
 #pragma unroll
-      for (int q = 0; q < QPB; ++q) {
-        const f16x4 h = __builtin_bit_cast(f16x4, v[u][q]);
+    for (int q = 0; q < QPB; ++q) {
+      const f16x4 h = __builtin_bit_cast(f16x4, v[u][q]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[q][i] = __builtin_fmaf(c, (float)h[i], acc[q][i]);
-      }
+      for (int i = 0; i < 4; ++i) acc[q][i] = __builtin_fmaf(c, (float)h[i], acc[q][i]);
     }
   }
 #pragma unroll
@@ -1046,7 +1057,9 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
 #pragma unroll
     for (int i = 1; i < RED_WAVES; ++i) tot += part[i][qq][lane];
     float W = 0.f;
-    const uint32_t Sr = any_bad ? 1u : 0u;
+    uint32_t Sr = 0u;
+#pragma unroll
+    for (int i = 0; i < RED_WAVES; ++i) Sr |= bad_w[i];
     float Mr = red_m[0][prow];
 #pragma unroll
     for (int i = 0; i < RED_SG; ++i) {
