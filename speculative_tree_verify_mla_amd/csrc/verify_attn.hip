@@ -162,12 +162,11 @@ struct ReduceArgs {
 // whose slot is outside the pool: a row of zeros.
 __device__ const uint16_t va_zero_row[DQK] = {};
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two fp32 values as packed bf16 bits (a in the low half), rounded to
+// nearest even by the hardware conversion.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -986,8 +985,15 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
   const u32x2* src = reinterpret_cast<const u32x2*>(part_o) + wbase * PART_VEC + piece * 64;
   const int64_t split_step = (int64_t)G * PART_VEC;
   float2 lv[RED_LSE];
+  {
+    const float2* const last = plse + (ns - 1) * lse_step;
+    const float2* lp = plse + sg * lse_step;
 #pragma unroll
-  for (int i = 0; i < RED_LSE; ++i) lv[i] = plse[min(sg + i * RED_SG, ns - 1) * lse_step];
+    for (int i = 0; i < RED_LSE; ++i) {
+      lv[i] = *(sg + i * RED_SG < ns ? lp : last);
+      lp += RED_SG * lse_step;
+    }
+  }
   const uint32_t st = status[wbase + (int64_t)min(tid, ns - 1) * G];
   u32x2 v[RED_PER_WAVE][QPB];
   {
@@ -1004,10 +1010,11 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
     }
   }
 
-  // per-row max over the splits
-  float m = -INFINITY;
+  // per-row max over the splits (the re-read copies of the last split
+  // leave it unchanged)
+  float m = lv[0].x;
 #pragma unroll
-  for (int i = 0; i < RED_LSE; ++i) m = sg + i * RED_SG < ns ? fmaxf(m, lv[i].x) : m;
+  for (int i = 1; i < RED_LSE; ++i) m = fmaxf(m, lv[i].x);
   red_m[sg][row] = m;
   // the status words: one flag per wave, read by the finishing waves after
   // the barriers below (a block-wide reduction would cost barriers of its own)
@@ -1018,15 +1025,17 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
 #pragma unroll
   for (int i = 1; i < RED_SG; ++i) M = fmaxf(M, red_m[i][row]);
   // coefficients and weight sums, without branches: splits past the
-  // request's last (s < MAXS, so inside the table) get coefficient 0
+  // request's last (s < MAXS, so inside the table) get coefficient 0, as do
+  // empty splits (lse -inf) and every split of a row without keys (M -inf).
+  // The hardware exp2 flushes weights below 2^-126 of the largest to 0.
+  const bool row_on = M != -INFINITY;
   float wsum = 0.f;
 #pragma unroll
   for (int i = 0; i < RED_LSE; ++i) {
     const int s = sg + i * RED_SG;
-    const bool on = s < ns && lv[i].x != -INFINITY && M != -INFINITY;
-    const float e = exp2f(on ? lv[i].x - M : -INFINITY);
+    const float e = __builtin_amdgcn_exp2f(s < ns && row_on ? lv[i].x - M : -INFINITY);
     wsum += e;
-    coef[s][row] = e > 0.f ? ldexpf(e, (int)lv[i].y) : 0.f;
+    coef[s][row] = ldexpf(e, (int)lv[i].y);
   }
   red_w[sg][row] = wsum;
   __syncthreads();
@@ -1056,16 +1065,13 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
     f32x4 tot = part[0][qq][lane];
 #pragma unroll
     for (int i = 1; i < RED_WAVES; ++i) tot += part[i][qq][lane];
+    // this thread's row is prow, whose max M it took above
     float W = 0.f;
     uint32_t Sr = 0u;
 #pragma unroll
     for (int i = 0; i < RED_WAVES; ++i) Sr |= bad_w[i];
-    float Mr = red_m[0][prow];
 #pragma unroll
-    for (int i = 0; i < RED_SG; ++i) {
-      W += red_w[i][prow];
-      Mr = fmaxf(Mr, red_m[i][prow]);
-    }
+    for (int i = 0; i < RED_SG; ++i) W += red_w[i][prow];
     const int rr = g * ROWS + rh * 32 + prow;   // row within the request
     if (rr < rows_r) {
       float res[4];
@@ -1076,15 +1082,16 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
       } else if (W > 0.f) {
         const float inv = 1.f / W;
         res[0] = tot[0] * inv; res[1] = tot[1] * inv; res[2] = tot[2] * inv; res[3] = tot[3] * inv;
-        lse_out = (Mr + log2f(W)) * LN2;
+        lse_out = (M + log2f(W)) * LN2;
       } else {
         res[0] = res[1] = res[2] = res[3] = 0.f;
         lse_out = -INFINITY;
       }
       const int64_t orow = (int64_t)tb * H + rr;
       const int col = cb * 32 + 8 * (qd + qq) + 4 * (lane >> 5);
-      const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[0]) | ((uint32_t)f32_to_bf16_rne(res[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[2]) | ((uint32_t)f32_to_bf16_rne(res[3]) << 16);
+      // round to nearest even (v_cvt_pk_bf16_f32)
+      const uint32_t lo = bf16_pair(res[0], res[1]);
+      const uint32_t hi = bf16_pair(res[2], res[3]);
       *reinterpret_cast<uint2*>(out + orow * DV + col) = make_uint2(lo, hi);
       if (((piece + qq) & (O_BLK * 4 - 1)) == 0 && lane < 32) lse[orow] = lse_out;   // once per row
     }
