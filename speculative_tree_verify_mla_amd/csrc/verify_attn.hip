@@ -1027,7 +1027,9 @@ __global__ __launch_bounds__(red_threads(MAXS)) void va_reduce_kernel(
   // coefficients and weight sums, without branches: splits past the
   // request's last (s < MAXS, so inside the table) get coefficient 0, as do
   // empty splits (lse -inf) and every split of a row without keys (M -inf).
-  // The hardware exp2 flushes weights below 2^-126 of the largest to 0.
+  // The hardware exp2 (no rescaling below 2^-126) may return 0 for weights
+  // under 2^-126 of the largest: a term that small moves the output only if
+  // the split's values exceed the output's by a factor near 2^126.
   const bool row_on = M != -INFINITY;
   float wsum = 0.f;
 #pragma unroll
