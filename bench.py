@@ -118,6 +118,39 @@ def capture_timer(torch, stream):
     return time_graph
 
 
+def capture_timer_interleaved(torch, stream):
+    """Returns time_graphs(fns, n, rounds): for each fn, the median over
+    `rounds` of ms per call of fn(i), i < n, each fn captured in its own HIP
+    graph; the graphs' timed replays alternate round by round, so a clock
+    that drifts under sustained load affects every fn alike."""
+    def time_graphs(fns, n, rounds):
+        graphs = []
+        for fn in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(n):
+                        fn(i)
+            torch.cuda.synchronize()
+            g.replay()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        times = [[] for _ in fns]
+        for r in range(rounds):
+            order = range(len(fns)) if r % 2 == 0 else reversed(range(len(fns)))
+            for k in order:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(stream):
+                    e0.record(stream)
+                    graphs[k].replay()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                times[k].append(e0.elapsed_time(e1) / n)
+        return [float(np.median(t)) for t in times]
+    return time_graphs
+
+
 def measure_defrag(torch, va, wl, pools, table, indptr, prefix, parent, q, H, K, stream,
                    time_graph):
     """Tier 1 defrag on the bench request: the compaction kernel's time, and
@@ -265,8 +298,9 @@ def measure_restart(torch, va, inputs, wl, pool, table, indptr, prefix, parent, 
 
 def measure_config(torch, va, inputs, dev, stream, idx, n_pools, steps):
     """One of the other workloads (full head count, ragged batch): µs per call
-    from a HIP graph of `steps` calls rotating over `n_pools` pool copies,
-    effective KV GB/s and MFMA use against the dense bf16 peak."""
+    from a HIP graph of `steps` calls rotating over `n_pools` pool copies (the
+    median of 5 rounds, alternating with the partial-only graph), effective KV
+    GB/s and MFMA use against the dense bf16 peak."""
     t0 = time.time()
     wl = inputs.make_config(idx)
 
@@ -296,9 +330,8 @@ def measure_config(torch, va, inputs, dev, stream, idx, n_pools, steps):
     torch.cuda.synchronize()
     if va.verify_attn_read_status(plan, ws, stream) != 0:
         raise RuntimeError(f"config {idx}: device status")
-    time_graph = capture_timer(torch, stream)
-    ms = time_graph(step, steps)
-    ms_partial = time_graph(lambda i: step(i, reduce=False), steps)
+    ms, ms_partial = capture_timer_interleaved(torch, stream)(
+        [step, lambda i: step(i, reduce=False)], steps, 5)
     n_row_keys = sum(int(T_r) * H * (int(L_r) + int(T_r))
                      for T_r, L_r in zip(wl.num_tree, wl.prefix_len))
     flops = 2.0 * n_row_keys * (576 + 512)
