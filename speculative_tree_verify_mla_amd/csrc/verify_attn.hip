@@ -920,9 +920,10 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
 // (SG = threads / 32), wave v the pieces of splits v, v + W, ...
 // (W = threads / 64), and thread i the status word of split i.  Loads past
 // the request's last split re-read that split (in bounds, no branch around
-// any load) and are dropped.  Then, on registers and LDS: the row max over
-// the splits, the coefficients exp2(lse_s - max) * 2^e_s, each wave's
-// weighted sum of its pieces, and the sum over the waves.
+// any load): they leave the row max unchanged and enter the sums with
+// coefficient 0.  Then, on registers and LDS: the row max over the splits,
+// the coefficients exp2(lse_s - max) * 2^e_s, each wave's weighted sum of
+// its pieces, and the sum over the waves.
 constexpr int RED_PIECES = 2 * O_BLK * 4;   // blocks per row group
 constexpr int red_threads(int maxs) { return maxs <= 64 ? 256 : 512; }
 
