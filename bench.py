@@ -225,7 +225,8 @@ def measure_defrag(torch, va, wl, pools, table, indptr, prefix, parent, q, H, K,
 def measure_marshal(torch, va, inputs, dev, time_graph):
     """Device draft-tree marshaling (verify order, parent array, ancestor
     masks, draft slot entries) for the bench request's shape and for a batch
-    of four 64-node trees."""
+    of four 64-node trees; also with the queries gathered into verify order,
+    as two launches and as one."""
     res = {}
     for name, num_tree, prefix in (("1x16", [16], [65536]), ("4x64", [64] * 4, [4096] * 4)):
         wl = inputs.make_workload("marshal", 8, num_tree, prefix, 1 << 18, seed=7,
@@ -246,6 +247,10 @@ def measure_marshal(torch, va, inputs, dev, time_graph):
 
         ms = time_graph(marshal_q, 200)
         res[f"us_{name}_with_q"] = round(ms * 1e3, 3)
+        # the same in one launch
+        ms = time_graph(lambda i: va.verify_attn_build_tree_rows(plan, rp, rs, pre, ind, tab,
+                                                                 q_raw, q_v), 200)
+        res[f"us_{name}_with_q_one_launch"] = round(ms * 1e3, 3)
     res["pages_host_tree_and_mask_ms"] = 1.98
     return res
 

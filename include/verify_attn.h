@@ -405,6 +405,30 @@ int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const
 int verify_attn_permute_rows(const va_plan* plan, const int32_t* perm, const uint16_t* src,
                              uint16_t* dst, int64_t row_elems, va_stream_t stream);
 
+/*
+ * verify_attn_build_tree_rows - verify_attn_build_tree and
+ * verify_attn_permute_rows in one launch (enqueue only), for the same
+ * reason: the draft tree and the verify-order rows of one step without a
+ * second dependent launch ("The Execution Phase", section "The Methodology:
+ * Evidence-Driven Engineering" measures the tree and mask build as host work
+ * of every step).
+ *
+ * Arguments as for verify_attn_build_tree, then src, dst and row_elems as
+ * for verify_attn_permute_rows; every output is as those two calls write it
+ * for a request whose status is 0.  For a flagged request its outputs are
+ * unspecified (dst rows are some source row of the request, or zeros),
+ * nothing is written outside its own ranges, and other requests are not
+ * affected.  The row gather ranks the request's nodes again in each gather
+ * block (the same ranking) rather than reading perm.
+ * Errors (host): VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_SHAPE, VA_ERR_ALIGN, VA_ERR_HIP.
+ */
+int verify_attn_build_tree_rows(const va_plan* plan, const int32_t* raw_parent,
+                                const int32_t* raw_slot, const int32_t* prefix_len,
+                                const int32_t* slot_indptr, int32_t* slot_table,
+                                int32_t slot_table_len, int32_t* perm, int32_t* parent,
+                                uint64_t* anc, uint32_t* status, const uint16_t* src,
+                                uint16_t* dst, int64_t row_elems, va_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     load_library,
     verify_attn,
     verify_attn_build_tree,
+    verify_attn_build_tree_rows,
     verify_attn_check_tree,
     verify_attn_compact,
     verify_attn_error_string,

@@ -42,7 +42,7 @@ EXPORTS = (
     "verify_attn_check_tree", "verify_attn_gather_rows", "verify_attn_stream_read",
     "verify_attn_error_string",
     "verify_attn_plan_struct_size", "verify_attn_compact_workspace_bytes", "verify_attn_compact",
-    "verify_attn_build_tree", "verify_attn_permute_rows",
+    "verify_attn_build_tree", "verify_attn_permute_rows", "verify_attn_build_tree_rows",
 )
 TREE_BITS = {1: "BAD_PARENT", 2: "BAD_TABLE"}
 COMPACT_BITS = {1: "BAD_SLOT", 2: "RUN_OCCUPIED"}
@@ -115,6 +115,9 @@ def load_library(path: os.PathLike | None = None):
     lib.verify_attn_build_tree.restype = ctypes.c_int
     lib.verify_attn_permute_rows.argtypes = [ctypes.POINTER(VaPlan), P, P, P, i64, P]
     lib.verify_attn_permute_rows.restype = ctypes.c_int
+    lib.verify_attn_build_tree_rows.argtypes = [ctypes.POINTER(VaPlan), P, P, P, P, P, i32, P, P, P,
+                                                P, P, P, i64, P]
+    lib.verify_attn_build_tree_rows.restype = ctypes.c_int
     lib.verify_attn_plan_struct_size.argtypes = []
     lib.verify_attn_plan_struct_size.restype = sz
     for name in ("verify_attn_plan", "verify_attn_plan_ex", "verify_attn_run", "verify_attn_reduce",
@@ -375,6 +378,39 @@ def verify_attn_permute_rows(plan, perm, src, dst=None, stream=None):
         _dptr(dst, b16, "dst"), int(src.numel() // n), _stream_handle(stream))
     _check("verify_attn_permute_rows", rc)
     return dst
+
+
+def verify_attn_build_tree_rows(plan, raw_parent, raw_slot, prefix_len, slot_indptr, slot_table,
+                                src, dst=None, stream=None):
+    """verify_attn_build_tree and verify_attn_permute_rows in one launch:
+    returns (perm, parent, anc, status, dst) as those two calls would."""
+    import torch
+    dev = raw_parent.device
+    n = int(plan.total_tree)
+    if raw_parent.numel() != n or raw_slot.numel() != n:
+        raise ValueError("raw_parent and raw_slot need sum(T_r) entries")
+    if src.shape[0] != n:
+        raise ValueError("src needs sum(T_r) rows")
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst.shape != src.shape:
+        raise ValueError("dst must have the shape of src")
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    parent = torch.empty(n, dtype=torch.int32, device=dev)
+    anc = torch.empty(n, dtype=torch.int64, device=dev)
+    status = torch.empty(int(plan.num_requests), dtype=torch.int32, device=dev)
+    i32 = (torch.int32,)
+    b16 = _bf16_types()
+    rc = load_library().verify_attn_build_tree_rows(
+        ctypes.byref(plan), _dptr(raw_parent, i32, "raw_parent"), _dptr(raw_slot, i32, "raw_slot"),
+        _dptr(prefix_len, i32, "prefix_len"), _dptr(slot_indptr, i32, "slot_indptr"),
+        _dptr(slot_table, i32, "slot_table"), int(slot_table.numel()),
+        _dptr(perm, i32, "perm"), _dptr(parent, i32, "parent"),
+        _dptr(anc, (torch.int64,), "anc"), _dptr(status, i32, "status"),
+        _dptr(src, b16, "src"), _dptr(dst, b16, "dst"), int(src.numel() // n),
+        _stream_handle(stream))
+    _check("verify_attn_build_tree_rows", rc)
+    return perm, parent, anc, status, dst
 
 
 # --------------------------------------------------------------------------- convenience

@@ -44,37 +44,23 @@ struct TreeArgs {
   int32_t tree_begin[VA_MAX_REQUESTS + 1];
 };
 
-// The inputs of the first loads come as leading scalar parameters, which the
-// library's build preloads into scalar registers (no kernel-argument load
-// before them); ONE (a single request) also takes its node count from there.
-template <bool ONE>
-__global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* raw_parent,
-                                                        const int32_t* raw_slot,
-                                                        const int32_t* prefix_len,
-                                                        const int32_t* slot_indptr,
-                                                        int32_t num_requests, int32_t t_first,
-                                                        TreeArgs a) {
-  const int r = blockIdx.x;
-  if (r >= num_requests) return;
-  const int lane = threadIdx.x;
-  const int t0 = ONE ? 0 : a.tree_begin[r];
-  const int T = ONE ? t_first : a.tree_begin[r + 1] - t0;
-  const bool live = lane < T;
-  uint32_t bad = 0u;
-
-  // depth by walking up the chain: every lane holds its node's parent (one
-  // load), and the walk follows the chains through the wave.  A parent out
-  // of range flags the request and ends the chains through that node; a
-  // walk still going after 64 steps (more than T) is a cycle.
-  // every load up front: the walk, the ranking and the table write then need
-  // no further round trip to memory
-  int p = live ? raw_parent[t0 + lane] : -1;
-  const int32_t my_slot = live ? raw_slot[t0 + lane] : 0;
-  const int32_t tab_base = slot_indptr[r];
-  const int64_t tab_lo = (int64_t)tab_base + prefix_len[r];
-  const int32_t tab_hi = slot_indptr[r + 1];
+// Verify position of raw node `lane` of a request (one 64-lane wave, lane j =
+// raw node j, live = j < T): the rank of (depth, raw index) among the live
+// nodes.  p is the node's parent (lane) after the range check, -1 for a
+// root; bad gets VA_TREE_BAD_PARENT for a parent outside [-1, T) or a cycle.
+// Depth comes from walking up the chains through the wave: every lane holds
+// its node's parent (one load), and a walk still going after 64 steps (more
+// than T) is a cycle.
+struct TreeRank {
+  int p;
+  int rank;
+  uint32_t bad;
+};
+__device__ __forceinline__ TreeRank tree_rank(int p, bool live, int T, int lane) {
+  TreeRank tr;
+  tr.bad = 0u;
   if (live && (p < -1 || p >= T)) {
-    bad = VA_TREE_BAD_PARENT;
+    tr.bad = VA_TREE_BAD_PARENT;
     p = -1;
   }
   int depth = 0;
@@ -87,12 +73,37 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* raw_paren
         x = nx;
       }
     }
-    if (x >= 0) bad = VA_TREE_BAD_PARENT;
+    if (x >= 0) tr.bad = VA_TREE_BAD_PARENT;
   }
-  // verify position = rank of (depth, raw index) among the live nodes
   const int key = live ? (depth << 6) | lane : 0x7fffffff;
   int rank = 0;
   for (int k = 0; k < 64; ++k) rank += __shfl(key, k) < key ? 1 : 0;
+  tr.p = p;
+  tr.rank = rank;
+  return tr;
+}
+
+// Request r's tree, on one 64-lane wave (lane = raw node).
+template <bool ONE>
+__device__ __forceinline__ void build_tree_body(const int32_t* raw_parent, const int32_t* raw_slot,
+                                                const int32_t* prefix_len,
+                                                const int32_t* slot_indptr, int r, int t_first,
+                                                const TreeArgs& a, int lane) {
+  const int t0 = ONE ? 0 : a.tree_begin[r];
+  const int T = ONE ? t_first : a.tree_begin[r + 1] - t0;
+  const bool live = lane < T;
+
+  // every load up front: the walk, the ranking and the table write then need
+  // no further round trip to memory
+  const int p_raw = live ? raw_parent[t0 + lane] : -1;
+  const int32_t my_slot = live ? raw_slot[t0 + lane] : 0;
+  const int32_t tab_base = slot_indptr[r];
+  const int64_t tab_lo = (int64_t)tab_base + prefix_len[r];
+  const int32_t tab_hi = slot_indptr[r + 1];
+  const TreeRank tr = tree_rank(p_raw, live, T, lane);
+  const int p = tr.p;
+  const int rank = tr.rank;
+  uint32_t bad = tr.bad;
   const int prank = __shfl(rank, p < 0 ? 0 : p);
   // ancestor mask in verify positions: walk the chain again, mapping raw ids
   // to verify positions through the wave (every lane takes part in the
@@ -127,6 +138,21 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* raw_paren
   if (lane == 0) a.status[r] = bits;
 }
 
+// The inputs of the first loads come as leading scalar parameters, which the
+// library's build preloads into scalar registers (no kernel-argument load
+// before them); ONE (a single request) also takes its node count from there.
+template <bool ONE>
+__global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* raw_parent,
+                                                        const int32_t* raw_slot,
+                                                        const int32_t* prefix_len,
+                                                        const int32_t* slot_indptr,
+                                                        int32_t num_requests, int32_t t_first,
+                                                        TreeArgs a) {
+  const int r = blockIdx.x;
+  if (r >= num_requests) return;
+  build_tree_body<ONE>(raw_parent, raw_slot, prefix_len, slot_indptr, r, t_first, a, threadIdx.x);
+}
+
 // dst row t0 + i = src row t0 + perm[t0 + i]: block (x, R) copies 16-byte
 // pieces 256 x .. 256 x + 255 of verify row R.  Pointers and sizes come as
 // leading (preloaded) arguments; ONE (a single request) needs no table.
@@ -157,6 +183,62 @@ __global__ __launch_bounds__(PERMUTE_THREADS) void permute_rows_kernel(
   dst[(int64_t)R * pieces + p] = v;
 }
 
+// Tree and row gather in one launch: blocks 0 .. B-1 build request b's tree
+// (wave 0, as build_tree_kernel); block B + x R + c gathers pieces
+// 256 c .. 256 c + 255 of verify row R (x blocks per row).  A gather block
+// needs the raw node at its verify position, so each of its waves ranks its
+// request's nodes again (the same tree_rank, on the same parent loads)
+// instead of waiting for the tree blocks: nothing passes between blocks.
+// The leading (preloaded) parameters are what a gather block needs first.
+template <bool ONE>
+__global__ __launch_bounds__(PERMUTE_THREADS) void build_tree_rows_kernel(
+    const int32_t* raw_parent, const int32_t* raw_slot, const int32_t* prefix_len,
+    const int32_t* slot_indptr, int32_t num_requests, int32_t xblocks, int32_t t_first,
+    int64_t pieces, const vec4u* src, vec4u* dst, TreeArgs a) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  if (b < num_requests) {
+    if (threadIdx.x < 64) build_tree_body<ONE>(raw_parent, raw_slot, prefix_len, slot_indptr, b,
+                                               t_first, a, lane);
+    return;
+  }
+  const int g = b - num_requests;
+  const int R = g / xblocks;   // verify row
+  const int c = g - R * xblocks;
+  int r = 0;
+  if (!ONE)
+    while (r + 1 < num_requests && a.tree_begin[r + 1] <= R) ++r;
+  const int t0 = ONE ? 0 : a.tree_begin[r];
+  const int T = ONE ? t_first : a.tree_begin[r + 1] - t0;
+  const bool live = lane < T;
+  const TreeRank tr = tree_rank(live ? raw_parent[t0 + lane] : -1, live, T, lane);
+  // the raw node ranked at position R - t0 (none, in a flagged request,
+  // gives a row of zeros)
+  const uint64_t at = __ballot(live && tr.rank == R - t0);
+  const int j = at ? __builtin_ctzll(at) : -1;
+  const int64_t p = (int64_t)c * PERMUTE_THREADS + threadIdx.x;
+  if (p >= pieces) return;
+  vec4u v = {0u, 0u, 0u, 0u};
+  // each source row is read once
+  if (j >= 0) v = __builtin_nontemporal_load(src + (int64_t)(t0 + j) * pieces + p);
+  dst[(int64_t)R * pieces + p] = v;
+}
+
+// Plan checks shared by the tree entry points: the kernels index the
+// caller's arrays through tree_begin, which must start at 0 and step by each
+// request's tree size, as the planner writes it.
+bool tree_plan_ok(const va_plan* plan) {
+  if (plan->magic != VA_PLAN_MAGIC || plan->version != VA_PLAN_VERSION ||
+      plan->num_requests < 1 || plan->num_requests > VA_MAX_REQUESTS || plan->tree_begin[0] != 0 ||
+      plan->total_tree != plan->tree_begin[plan->num_requests] || plan->total_tree < 1)
+    return false;
+  for (int r = 0; r < plan->num_requests; ++r)
+    if (plan->num_tree[r] < 1 || plan->num_tree[r] > VA_MAX_TREE ||
+        plan->tree_begin[r + 1] - plan->tree_begin[r] != plan->num_tree[r])
+      return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,16 +251,7 @@ int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const
       slot_indptr == nullptr || slot_table == nullptr || perm == nullptr || parent == nullptr ||
       anc == nullptr || status == nullptr)
     return VA_ERR_NULL;
-  // the kernel indexes the caller's arrays through tree_begin: it must start
-  // at 0 and step by each request's tree size, as the planner writes it
-  if (plan->magic != VA_PLAN_MAGIC || plan->version != VA_PLAN_VERSION ||
-      plan->num_requests < 1 || plan->num_requests > VA_MAX_REQUESTS || plan->tree_begin[0] != 0 ||
-      plan->total_tree != plan->tree_begin[plan->num_requests])
-    return VA_ERR_PLAN;
-  for (int r = 0; r < plan->num_requests; ++r)
-    if (plan->num_tree[r] < 1 || plan->num_tree[r] > VA_MAX_TREE ||
-        plan->tree_begin[r + 1] - plan->tree_begin[r] != plan->num_tree[r])
-      return VA_ERR_PLAN;
+  if (!tree_plan_ok(plan)) return VA_ERR_PLAN;
   if (slot_table_len < 0) return VA_ERR_SHAPE;
   TreeArgs a;
   a.slot_table = slot_table;
@@ -202,14 +275,7 @@ int verify_attn_build_tree(const va_plan* plan, const int32_t* raw_parent, const
 int verify_attn_permute_rows(const va_plan* plan, const int32_t* perm, const uint16_t* src,
                              uint16_t* dst, int64_t row_elems, va_stream_t stream) {
   if (plan == nullptr || perm == nullptr || src == nullptr || dst == nullptr) return VA_ERR_NULL;
-  if (plan->magic != VA_PLAN_MAGIC || plan->version != VA_PLAN_VERSION ||
-      plan->num_requests < 1 || plan->num_requests > VA_MAX_REQUESTS || plan->tree_begin[0] != 0 ||
-      plan->total_tree != plan->tree_begin[plan->num_requests] || plan->total_tree < 1)
-    return VA_ERR_PLAN;
-  for (int r = 0; r < plan->num_requests; ++r)
-    if (plan->num_tree[r] < 1 || plan->num_tree[r] > VA_MAX_TREE ||
-        plan->tree_begin[r + 1] - plan->tree_begin[r] != plan->num_tree[r])
-      return VA_ERR_PLAN;
+  if (!tree_plan_ok(plan)) return VA_ERR_PLAN;
   if (row_elems < 8 || (row_elems % 8) != 0 || row_elems > ((int64_t)1 << 40)) return VA_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15u) != 0)
     return VA_ERR_ALIGN;
@@ -229,6 +295,47 @@ int verify_attn_permute_rows(const va_plan* plan, const int32_t* perm, const uin
   else
     hipLaunchKernelGGL(permute_rows_kernel<false>, grid, dim3(PERMUTE_THREADS), 0, st, perm, s4,
                        d4, pieces, plan->num_tree[0], a);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+int verify_attn_build_tree_rows(const va_plan* plan, const int32_t* raw_parent,
+                                const int32_t* raw_slot, const int32_t* prefix_len,
+                                const int32_t* slot_indptr, int32_t* slot_table,
+                                int32_t slot_table_len, int32_t* perm, int32_t* parent,
+                                uint64_t* anc, uint32_t* status, const uint16_t* src,
+                                uint16_t* dst, int64_t row_elems, va_stream_t stream) {
+  if (plan == nullptr || raw_parent == nullptr || raw_slot == nullptr || prefix_len == nullptr ||
+      slot_indptr == nullptr || slot_table == nullptr || perm == nullptr || parent == nullptr ||
+      anc == nullptr || status == nullptr || src == nullptr || dst == nullptr)
+    return VA_ERR_NULL;
+  if (!tree_plan_ok(plan)) return VA_ERR_PLAN;
+  if (slot_table_len < 0) return VA_ERR_SHAPE;
+  if (row_elems < 8 || (row_elems % 8) != 0 || row_elems > ((int64_t)1 << 40)) return VA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15u) != 0)
+    return VA_ERR_ALIGN;
+  const int64_t pieces = row_elems / 8;
+  const int64_t xblocks = (pieces + PERMUTE_THREADS - 1) / PERMUTE_THREADS;
+  const int64_t blocks = plan->num_requests + xblocks * plan->total_tree;
+  if (blocks > INT32_MAX) return VA_ERR_SHAPE;
+  TreeArgs a;
+  a.slot_table = slot_table;
+  a.slot_table_len = slot_table_len;
+  a.perm = perm;
+  a.parent = parent;
+  a.anc = anc;
+  a.status = status;
+  for (int r = 0; r <= plan->num_requests; ++r) a.tree_begin[r] = plan->tree_begin[r];
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const vec4u* s4 = reinterpret_cast<const vec4u*>(src);
+  vec4u* d4 = reinterpret_cast<vec4u*>(dst);
+  if (plan->num_requests == 1)
+    hipLaunchKernelGGL(build_tree_rows_kernel<true>, dim3((unsigned)blocks), dim3(PERMUTE_THREADS),
+                       0, st, raw_parent, raw_slot, prefix_len, slot_indptr, plan->num_requests,
+                       (int32_t)xblocks, plan->num_tree[0], pieces, s4, d4, a);
+  else
+    hipLaunchKernelGGL(build_tree_rows_kernel<false>, dim3((unsigned)blocks), dim3(PERMUTE_THREADS),
+                       0, st, raw_parent, raw_slot, prefix_len, slot_indptr, plan->num_requests,
+                       (int32_t)xblocks, plan->num_tree[0], pieces, s4, d4, a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 

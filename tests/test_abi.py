@@ -299,6 +299,9 @@ def test_build_tree_refuses_tampered_plans_before_launch(field, value):
                                       f(4096), 100, f(4096), f(4096), f(4096), f(4096), None) == -5
     assert lib.verify_attn_permute_rows(ctypes.byref(bad), f(4096), f(4096), f(8192), 4608,
                                         None) == -5
+    assert lib.verify_attn_build_tree_rows(ctypes.byref(bad), f(4096), f(4096), f(4096), f(4096),
+                                           f(4096), 100, f(4096), f(4096), f(4096), f(4096),
+                                           f(4096), f(8192), 4608, None) == -5
 
 
 def test_permute_rows_argument_errors_before_launch():
@@ -316,3 +319,27 @@ def test_permute_rows_argument_errors_before_launch():
     assert lib.verify_attn_permute_rows(p, f(4096), f(4096), f(8192), 0, None) == -2
     assert lib.verify_attn_permute_rows(p, f(4096), f(4104), f(8192), 4608, None) == -3   # src
     assert lib.verify_attn_permute_rows(p, f(4096), f(4096), f(8200), 4608, None) == -3   # dst
+
+
+def test_build_tree_rows_argument_errors_before_launch():
+    """verify_attn_build_tree_rows checks its arguments on the host; every case
+    here returns before a launch (so no GPU)."""
+    lib = va.load_library()
+    plan = _plan(8, [100, 50], [4, 6])
+    f = _fake
+    p = ctypes.byref(plan)
+
+    def call(*over):
+        args = [p, f(4096), f(4096), f(4096), f(4096), f(4096), 100, f(4096), f(4096), f(4096),
+                f(4096), f(4096), f(8192), 4608, None]
+        for i, v in over:
+            args[i] = v
+        return lib.verify_attn_build_tree_rows(*args)
+
+    for i in (0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12):   # every pointer argument
+        assert call((i, None)) == -1, i
+    assert call((6, -1)) == -2                  # slot_table_len
+    assert call((13, 4607)) == -2               # row_elems not a multiple of 8
+    assert call((13, 0)) == -2
+    assert call((11, f(4104))) == -3            # src not 16-byte aligned
+    assert call((12, f(8200))) == -3            # dst

@@ -185,3 +185,117 @@ def test_permute_rows_gathers_through_perm():
                     want[t0 + i] = srch[t0 + j]
             t0 += t
         np.testing.assert_array_equal(got, want)
+
+
+def _gather_rows(num_tree, perm, rows):
+    """Host gather: row t0 + i of the result is rows[t0 + perm[t0 + i]]."""
+    out = np.empty_like(rows)
+    t0 = 0
+    for t in num_tree:
+        out[t0:t0 + t] = rows[t0:t0 + t][perm[t0:t0 + t]]
+        t0 += t
+    return out
+
+
+@pytest.mark.parametrize("num_tree,prefix", [([1], [10]), ([16], [300]), ([64], [1000]),
+                                             ([3, 33, 1, 64], [5, 70, 0, 400])])
+def test_build_tree_rows_matches_the_reference(num_tree, prefix):
+    """verify_attn_build_tree_rows (tree and query gather in one launch): the
+    marshaled outputs against oracle.tree and the gathered query rows against
+    a host gather through the oracle's perm, bit for bit."""
+    wl, rp, rs, q_raw = _raw_batch(num_tree, prefix, seed=3 + sum(num_tree))
+    table = wl.slot_table.copy()
+    for r in range(len(num_tree)):
+        b = int(wl.slot_indptr[r]) + int(wl.prefix_len[r])
+        table[b:b + num_tree[r]] = -7
+    ref = ot.marshal(wl.num_tree, rp, rs, wl.prefix_len, wl.slot_indptr, table)
+    plan = va.verify_attn_plan(wl.num_heads, wl.prefix_len, wl.num_tree)
+    tab = _t(table)
+    qr = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    perm, parent, anc, status, qv = va.verify_attn_build_tree_rows(
+        plan, _t(rp), _t(rs), _t(wl.prefix_len), _t(wl.slot_indptr), tab, qr)
+    torch.cuda.synchronize()
+    got = (perm.cpu().numpy(), parent.cpu().numpy(), anc.cpu().numpy().view(np.uint64),
+           status.cpu().numpy().view(np.uint32), tab.cpu().numpy())
+    say(f"  build_tree_rows T={num_tree} status={got[3].tolist()}")
+    assert (got[3] == 0).all()
+    for k in range(5):
+        np.testing.assert_array_equal(got[k], ref[k])
+    want = _gather_rows(num_tree, ref[0], q_raw.view(np.int16))
+    np.testing.assert_array_equal(qv.view(torch.int16).cpu().numpy(), want)
+
+
+def test_build_tree_rows_flags_bad_requests_and_keeps_the_rest_exact():
+    """A cycle and an out-of-range parent flag their requests as the two-call
+    path does; the good request's outputs and rows stay exact, and a flagged
+    request's rows are each one of its own raw rows or zeros."""
+    wl, rp, rs, q_raw = _raw_batch([6, 6, 6], [20, 30, 40], seed=11)
+    rp = rp.copy()
+    rp[0:2] = [1, 0]                      # request 0: a cycle
+    rp[6 + 3] = 6                         # request 1: parent out of range
+    ref = ot.marshal(wl.num_tree, rp, rs, wl.prefix_len, wl.slot_indptr, wl.slot_table)
+    plan = va.verify_attn_plan(wl.num_heads, wl.prefix_len, wl.num_tree)
+    tab = _t(wl.slot_table.copy())
+    qr = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    perm, parent, anc, status, qv = va.verify_attn_build_tree_rows(
+        plan, _t(rp), _t(rs), _t(wl.prefix_len), _t(wl.slot_indptr), tab, qr)
+    torch.cuda.synchronize()
+    st = status.cpu().numpy().view(np.uint32)
+    assert st[0] & ot.BAD_PARENT and st[1] & ot.BAD_PARENT and st[2] == 0
+    got = (perm.cpu().numpy(), parent.cpu().numpy(), anc.cpu().numpy().view(np.uint64))
+    for k in range(3):
+        np.testing.assert_array_equal(got[k][12:], ref[k][12:])
+    rows = qv.view(torch.int16).cpu().numpy()
+    qi = q_raw.view(np.int16)
+    np.testing.assert_array_equal(rows[12:], _gather_rows([6], ref[0][12:], qi[12:]))
+    for r in range(2):
+        own = qi[6 * r:6 * r + 6]
+        for i in range(6):
+            row = rows[6 * r + i]
+            assert not row.any() or any(np.array_equal(row, o) for o in own)
+
+
+def test_build_tree_rows_then_verify_in_one_graph():
+    """The one-launch marshaling and the verify call captured in one HIP graph,
+    replayed three times with eager work and a synchronisation between the
+    replays: every replay's output matches the oracle on the marshaled inputs."""
+    wl, rp, rs, q_raw = _raw_batch([16, 9], [700, 1200], seed=23)
+    d = Dev(wl)
+    table = wl.slot_table.copy()
+    for r in range(2):
+        b = int(wl.slot_indptr[r]) + int(wl.prefix_len[r])
+        table[b:b + int(wl.num_tree[r])] = -7
+    d.table = _t(table)
+    plan = va.verify_attn_plan(wl.num_heads, wl.prefix_len, wl.num_tree)
+    ws = va.workspace_for(plan, DEV)
+    raw_p, raw_s = _t(rp), _t(rs)
+    qr = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    qv = torch.empty_like(qr)
+    H = wl.num_heads
+    out = torch.empty((25, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((25, H), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            perm, parent, anc, status, _ = va.verify_attn_build_tree_rows(
+                plan, raw_p, raw_s, d.prefix, d.indptr, d.table, qr, qv, stream=st)
+            va.verify_attn(qv, d.kv, d.table, d.indptr, d.prefix, parent, wl.sm_scale,
+                           num_tree=wl.num_tree, prefix_len_host=wl.prefix_len, plan=plan,
+                           workspace=ws, out=out, lse=lse, stream=st)
+    torch.cuda.current_stream().wait_stream(st)
+    ref = ot.marshal(wl.num_tree, rp, rs, wl.prefix_len, wl.slot_indptr, table)
+    perm_h = ref[0]
+    q_v = np.concatenate([q_raw[:16][perm_h[:16]], q_raw[16:][perm_h[16:]]])
+    wl_v = inputs.Workload(**{**wl.__dict__, "q": q_v, "parent": ref[1], "slot_table": ref[4]})
+    for rep in range(3):
+        out.zero_()
+        qv.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert (status.cpu().numpy() == 0).all()
+        np.testing.assert_array_equal(d.table.cpu().numpy(), ref[4])
+        check(wl_v, out, lse, what=f"build_tree_rows+verify graph, replay {rep}")
