@@ -21,7 +21,8 @@
 // then unspecified, and nothing is written outside the request's own ranges.
 //
 // permute_rows_kernel then gathers per-node rows (the queries, H x 576 bf16
-// per node) from raw order into verify order through perm.
+// per node) from raw order into verify order through perm;
+// build_tree_rows_kernel does both in one launch.
 
 #include <hip/hip_runtime.h>
 
