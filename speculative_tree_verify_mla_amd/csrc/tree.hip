@@ -76,9 +76,19 @@ __device__ __forceinline__ TreeRank tree_rank(int p, bool live, int T, int lane)
     }
     if (x >= 0) tr.bad = VA_TREE_BAD_PARENT;
   }
-  const int key = live ? (depth << 6) | lane : 0x7fffffff;
+  // rank: the live nodes at a smaller depth, plus those at the same depth
+  // with a smaller raw index, one ballot per depth level (depths are at most
+  // 64, so the loop ends by then even for a cycle)
+  const uint64_t below = lane == 0 ? 0ull : ~0ull >> (64 - lane);
+  const int n_live = __popcll(__ballot(live));
   int rank = 0;
-  for (int k = 0; k < 64; ++k) rank += __shfl(key, k) < key ? 1 : 0;
+  int counted = 0;
+  for (int d = 0; d <= VA_MAX_TREE && counted < n_live; ++d) {   // uniform
+    const uint64_t at = __ballot(live && depth == d);
+    if (depth > d) rank += __popcll(at);
+    else if (depth == d) rank += __popcll(at & below);
+    counted += __popcll(at);
+  }
   tr.p = p;
   tr.rank = rank;
   return tr;
