@@ -299,3 +299,44 @@ def test_build_tree_rows_then_verify_in_one_graph():
         assert (status.cpu().numpy() == 0).all()
         np.testing.assert_array_equal(d.table.cpu().numpy(), ref[4])
         check(wl_v, out, lse, what=f"build_tree_rows+verify graph, replay {rep}")
+
+
+def test_build_tree_rows_equals_the_two_calls_on_random_batches():
+    """Random forests (1..6 requests of 1..64 nodes, any node order) and row
+    widths whose last gather block is partial: the one-launch call writes
+    exactly what verify_attn_build_tree + verify_attn_permute_rows write."""
+    rng = np.random.default_rng(2024)
+    for case in range(12):
+        B = int(rng.integers(1, 7))
+        num_tree = [int(x) for x in rng.integers(1, 65, size=B)]
+        H = int(rng.choice([1, 3, 8]))
+        prefix = [int(x) for x in rng.integers(0, 500, size=B)]
+        raw_parent = []
+        for t in num_tree:
+            # parent of node j among nodes placed before it, then shuffled
+            par = [-1] + [int(rng.integers(-1, j)) for j in range(1, t)]
+            sigma = rng.permutation(t)
+            rp = np.empty(t, np.int32)
+            for j in range(t):
+                rp[sigma[j]] = -1 if par[j] < 0 else sigma[par[j]]
+            raw_parent.append(rp)
+        raw_parent = np.concatenate(raw_parent).astype(np.int32)
+        n = len(raw_parent)
+        raw_slot = rng.integers(0, 1 << 20, size=n).astype(np.int32)
+        indptr = np.concatenate([[0], np.cumsum(np.asarray(prefix) + np.asarray(num_tree) + 3)]).astype(np.int32)
+        table = rng.integers(0, 1 << 20, size=int(indptr[-1])).astype(np.int32)
+        plan = va.verify_attn_plan(H, prefix, num_tree)
+        src = rng.standard_normal((n, H, 576)).astype(np.float32)
+        src_b = torch.from_numpy(inputs.bf16_bits(src).view(np.int16)).to(DEV).view(torch.bfloat16)
+        t1, t2 = _t(table), _t(table)
+        a = va.verify_attn_build_tree(plan, _t(raw_parent), _t(raw_slot), _t(np.asarray(prefix, np.int32)),
+                                      _t(indptr), t1)
+        rows_a = va.verify_attn_permute_rows(plan, a[0], src_b)
+        b = va.verify_attn_build_tree_rows(plan, _t(raw_parent), _t(raw_slot),
+                                           _t(np.asarray(prefix, np.int32)), _t(indptr), t2, src_b)
+        torch.cuda.synchronize()
+        assert (a[3].cpu().numpy() == 0).all() and (b[3].cpu().numpy() == 0).all()
+        for x, y in zip(a, b[:4]):
+            assert torch.equal(x, y), case
+        assert torch.equal(t1, t2), case
+        assert torch.equal(rows_a.view(torch.int16), b[4].view(torch.int16)), case
