@@ -356,6 +356,7 @@ def measure_config(torch, va, inputs, dev, stream, idx, n_pools, steps):
                                        / BF16_DENSE_PEAK_TFLOPS, 2),
         "nsplit": plan.splits(),
         "work_items": int(plan.total_work),
+        "rows_per_block": 64 * int(plan.groups_per_block),
         "pools_rotated": n_pools,
         "steps": steps,
     }
@@ -648,9 +649,10 @@ def main():
         "warm_value": round(kv_bytes / (ms_warm * 1e-3) / 1e9, 2),
         "nsplit": plan.splits(),
         "work_items": int(plan.total_work),
+        "rows_per_block": 64 * int(plan.groups_per_block),
         "kv_bytes_per_call": kv_bytes,
         "roofline": {
-            "kernel": "va_partial_kernel",
+            "kernel": "va_wide_kernel" if plan.groups_per_block == 2 else "va_partial_kernel",
             "bound": roofline_bound(flops, kv_bytes),
             "arith_intensity_flop_per_byte": round(flops / kv_bytes, 1),
             "ridge_flop_per_byte": round(BF16_DENSE_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS, 1),

@@ -97,7 +97,7 @@ typedef struct va_plan {
   int32_t total_rows;        /* sum of T_r * H */
   int32_t num_cus;           /* compute units the plan was sized for */
   int32_t mode;              /* VA_MODE_FUSED or VA_MODE_SPLIT_TREE */
-  int32_t reserved;          /* zero */
+  int32_t groups_per_block;  /* row groups one partial-pass block holds: 1, or 2 (128-row blocks) */
   int64_t workspace_bytes;   /* bytes verify_attn_run needs */
   int64_t lse_offset;        /* byte offset of the partial-lse region */
   int64_t status_offset;     /* byte offset of the per-work-item status words */
@@ -110,7 +110,7 @@ typedef struct va_plan {
 } va_plan;
 
 #define VA_PLAN_MAGIC 0x56415054u /* "VAPT" */
-#define VA_PLAN_VERSION 2u
+#define VA_PLAN_VERSION 3u
 
 /* How verify_attn_run decomposes the keys of a request (va_plan.mode).
  * VA_MODE_FUSED: one partial kernel; its nsplit splits cover equal slices
@@ -129,6 +129,8 @@ typedef struct va_plan {
 
 /* verify_attn_plan_ex flags */
 #define VA_PLAN_SPLIT_TREE 1u   /* plan VA_MODE_SPLIT_TREE instead of VA_MODE_FUSED */
+#define VA_PLAN_ROWS64 2u       /* 64-row blocks (groups_per_block = 1) whatever the row count */
+#define VA_PLAN_ROWS128 4u      /* 128-row blocks (groups_per_block = 2); one request, fused mode only */
 
 /*
  * verify_attn_plan - size the split-KV schedule and the workspace (host only).
@@ -154,6 +156,12 @@ typedef struct va_plan {
  * the compute units.  The environment variable VA_NSPLIT, read here
  * only, forces one split count for every request (for tuning sweeps; with
  * VA_PLAN_SPLIT_TREE it is the count of prefix splits).
+ * A single request in the fused mode with T*H >= 1024 rows gets 128-row
+ * blocks (groups_per_block = 2): one block runs the two row groups 2j and
+ * 2j+1 of a split, so each KV row enters a compute unit once per 128 rows,
+ * and the splits are balanced over ceil(groups / 2) blocks per split (about
+ * twice the splits of 64-row blocks).  The work items, the workspace and the
+ * merge stay those of 64-row groups.
  * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_HIP (device query failed).
  */
 int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
@@ -164,8 +172,11 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
  * verify_attn_plan_ex - verify_attn_plan with flags.  flags = 0 is
  * verify_attn_plan (VA_MODE_FUSED); VA_PLAN_SPLIT_TREE plans the
  * split-verify decomposition (VA_MODE_SPLIT_TREE): nsplit[r] counts the
- * prefix splits plus the one tree-block split.  Unknown flag bits are
- * VA_ERR_SHAPE.  Other arguments and errors as verify_attn_plan.
+ * prefix splits plus the one tree-block split.  VA_PLAN_ROWS64 and
+ * VA_PLAN_ROWS128 override the row-count rule for the block size; both
+ * together, or VA_PLAN_ROWS128 with more than one request or with
+ * VA_PLAN_SPLIT_TREE, are VA_ERR_SHAPE, as are unknown flag bits.  Other
+ * arguments and errors as verify_attn_plan.
  */
 int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
                         const int32_t* h_num_tree, int32_t num_cus, uint32_t flags,
@@ -229,9 +240,10 @@ int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out
  *
  * Arguments as verify_attn_run and verify_attn_reduce; out and lse as
  * verify_attn_reduce.  The scratch holds VA_STATIC_SCRATCH_BYTES, enough for
- * VA_STATIC_SCRATCH_WORK work items (any plan with plan->total_work <= 256,
- * e.g. every single-request plan for up to 256 compute units); a plan whose
- * workspace_bytes exceeds it is refused with VA_ERR_WORKSPACE.
+ * VA_STATIC_SCRATCH_WORK work items (any plan with plan->total_work <= 512,
+ * e.g. every single-request plan for up to 256 compute units with
+ * T*H <= 16,384 rows); a plan whose workspace_bytes exceeds it is refused
+ * with VA_ERR_WORKSPACE.
  * The first call on a device looks up that device's copy of the array
  * (hipGetSymbolAddress, with the device current); no call allocates.
  * Every call on one device shares its array: calls whose kernels may
@@ -243,9 +255,9 @@ int verify_attn_reduce(const va_plan* plan, const void* workspace, uint16_t* out
  * Errors: VA_ERR_NULL, VA_ERR_PLAN, VA_ERR_SHAPE, VA_ERR_ALIGN,
  *         VA_ERR_WORKSPACE (plan too large for the scratch), VA_ERR_HIP.
  */
-#define VA_STATIC_SCRATCH_WORK 256
-/* 256 work items x (65,536 B partials + 512 B lse pairs) + 1,024 B status words */
-#define VA_STATIC_SCRATCH_BYTES 16909312
+#define VA_STATIC_SCRATCH_WORK 512
+/* 512 work items x (65,536 B partials + 512 B lse pairs) + 2,048 B status words */
+#define VA_STATIC_SCRATCH_BYTES 33818624
 int verify_attn_forward_static(const va_plan* plan, const uint16_t* q, const uint16_t* kv_pool,
                                int64_t num_slots, int32_t kv_row_stride,
                                const int32_t* slot_table, int32_t slot_table_len,

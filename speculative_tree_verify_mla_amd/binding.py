@@ -23,10 +23,12 @@ VA_MAX_TREE = 64
 VA_MAX_REQUESTS = 64
 VA_MAX_SPLITS = 256
 VA_PLAN_MAGIC = 0x56415054
-VA_PLAN_VERSION = 2
+VA_PLAN_VERSION = 3
 VA_MODE_FUSED = 0
 VA_MODE_SPLIT_TREE = 1
 VA_PLAN_SPLIT_TREE = 1
+VA_PLAN_ROWS64 = 2
+VA_PLAN_ROWS128 = 4
 
 VA_OK = 0
 ERRORS = {
@@ -56,7 +58,7 @@ class VaPlan(ctypes.Structure):
         ("rows_per_group", ctypes.c_int32), ("tile_keys", ctypes.c_int32),
         ("total_work", ctypes.c_int32), ("total_tree", ctypes.c_int32),
         ("total_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-        ("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("mode", ctypes.c_int32), ("groups_per_block", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64), ("lse_offset", ctypes.c_int64),
         ("status_offset", ctypes.c_int64),
         ("num_tree", ctypes.c_int32 * VA_MAX_REQUESTS),
@@ -165,10 +167,13 @@ def _bf16_types():
 
 
 # --------------------------------------------------------------------------- C ABI mirrors
-def verify_attn_plan(num_heads, prefix_len, num_tree, num_cus=0, split_tree=False) -> VaPlan:
+def verify_attn_plan(num_heads, prefix_len, num_tree, num_cus=0, split_tree=False,
+                     rows=None) -> VaPlan:
     """Host-only plan.  prefix_len / num_tree: per-request host sequences.
-    split_tree=True plans the split-verify decomposition (verify_attn_plan_ex
-    with VA_PLAN_SPLIT_TREE); otherwise verify_attn_plan."""
+    split_tree=True plans the split-verify decomposition (VA_PLAN_SPLIT_TREE);
+    rows=64 or 128 fixes the partial pass's block size (VA_PLAN_ROWS64 /
+    VA_PLAN_ROWS128), rows=None leaves it to the planner.  Without flags this
+    is verify_attn_plan, otherwise verify_attn_plan_ex."""
     pl = _i32_host(prefix_len)
     nt = _i32_host(num_tree)
     if pl.shape != nt.shape:
@@ -177,9 +182,14 @@ def verify_attn_plan(num_heads, prefix_len, num_tree, num_cus=0, split_tree=Fals
     ws = ctypes.c_size_t(0)
     args = (int(nt.shape[0]), int(num_heads), pl.ctypes.data_as(ctypes.c_void_p),
             nt.ctypes.data_as(ctypes.c_void_p), int(num_cus))
+    flags = VA_PLAN_SPLIT_TREE if split_tree else 0
+    if rows is not None:
+        if rows not in (64, 128):
+            raise ValueError("rows must be None, 64 or 128")
+        flags |= VA_PLAN_ROWS64 if rows == 64 else VA_PLAN_ROWS128
     lib = load_library()
-    if split_tree:
-        rc = lib.verify_attn_plan_ex(*args, VA_PLAN_SPLIT_TREE, ctypes.byref(plan), ctypes.byref(ws))
+    if flags:
+        rc = lib.verify_attn_plan_ex(*args, flags, ctypes.byref(plan), ctypes.byref(ws))
         _check("verify_attn_plan_ex", rc)
     else:
         rc = lib.verify_attn_plan(*args, ctypes.byref(plan), ctypes.byref(ws))

@@ -908,6 +908,476 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
   if (tid == 0) a.status[w] = status_sh;
 }
 
+// ---- 128-row blocks over 32-key tiles (one request, fused mode) -----------
+// The streaming design loads each KV tile once and computes every head on it
+// ("The Execution Phase", section "The Core Design: A Streaming Flash
+// Attention Kernel").  With many rows per request (T * H >= WIDE_MIN_ROWS) a
+// block here takes the two 64-row work items of a split that share a row
+// pair (groups 2 gw and 2 gw + 1), so every KV row of the split enters the
+// CU once for 128 rows instead of once per 64.  Wave w owns rows
+// 32 w .. 32 w + 31 of the block entirely: the score of every key of a tile
+// over all 576 columns (Q k-steps 0 .. QV-1 in VGPRs, the rest from LDS),
+// its own softmax, and all 512 output columns (accumulators in the 256
+// AGPRs).  No probabilities change hands, so a tile needs one barrier.
+// Three 32-key tile buffers keep two tiles in flight.  The partials are
+// written as the two 64-row work items in the layout of va_partial_kernel,
+// so the merge is the same.
+//
+// The value products are inline-asm MFMAs that accumulate in AGPRs: the
+// compiler's hazard tracking does not see them, so the accumulators are
+// zeroed and read only behind acc_settle, which gives the wait states and
+// ties every later access of the accumulators to that point, and the
+// probabilities (written by VALU instructions) get their wait states before
+// the first value MFMA reads them.
+constexpr int WROWS = 128;
+constexpr int WIDE_MIN_ROWS = 1024;   // rows per request from which the planner picks these blocks
+constexpr int WTILE = 32;
+constexpr int WLINE = (WTILE / 8) * CHUNK;      // one line of all keys of a tile: 4 KB
+constexpr int WBUF_BYTES = NLINE * WLINE;       // 36,864 B
+constexpr int WBUF_ELEMS = WBUF_BYTES / 2;
+constexpr int WNBUF = 3;                        // two tiles in flight while one is consumed
+constexpr int WCOPIES = NLINE;                  // copies per wave per tile: 9 lines of its 8 keys
+constexpr int WSLOT_RING = 4;
+constexpr int QV = 24;   // score k-steps whose Q fragments stay in VGPRs; the rest are read from LDS
+
+struct WideSmem {
+  __attribute__((aligned(16))) uint16_t tiles[WNBUF * WBUF_ELEMS];
+  // Q fragments of score k-steps QV .. 35 per wave, [wave][k - QV][lane]
+  __attribute__((aligned(16))) bf16x8 qt[4][QK_STEPS - QV][64];
+  int32_t sring[WSLOT_RING][WTILE];
+  int32_t parents[64];
+  uint64_t anc[VA_MAX_TREE];
+  uint32_t status_sh;
+  uint32_t restart_sh[2];   // set by tile t's waves in entry t % 2, read after the next barrier
+};
+
+__device__ __forceinline__ constexpr int wpiece_off(int k, int p) {
+  return (p >> 3) * WLINE + (k >> 3) * CHUNK + (k & 7) * 128 + (((p & 7) ^ swz(k)) << 4);
+}
+// copy of line J of the wave's 8 keys: m0 = lds_w + (WLINE - 128) J, with the
+// instruction offset 128 J advancing both addresses
+template <int J>
+__device__ __forceinline__ void wdma_line(uint32_t lds_w, const void* addr) {
+  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3 nt"
+               :: "s"(lds_w), "v"(addr), "n"((WLINE - 128) * J), "n"(128 * J)
+               : "memory", "m0", "scc");
+}
+template <int... J>
+__device__ __forceinline__ void wdma_copy(int c, uint32_t lds_w, const void* addr,
+                                          std::integer_sequence<int, J...>) {
+  ((c == J ? wdma_line<J>(lds_w, addr) : void()), ...);
+}
+// 16 bytes per lane from a per-lane address (lane i writes lds + 16 i)
+__device__ __forceinline__ void dma16v(uint32_t lds, const void* addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(addr) : "memory", "m0");
+}
+// Wait states after the accumulating MFMAs (inline asm, which the compiler's
+// hazard tracking does not see) before any other instruction touches the
+// accumulators: the operands tie every later access of o to this point.
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[O_BLK]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                 "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+}
+// O^T block += V^T fragment . P^T fragment, accumulating in AGPRs
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, int block,
+                                          WideSmem& sm) {
+  uint16_t* const tiles = sm.tiles;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31;
+  const int lh = lane >> 5;
+
+  // blocks ordered (split, row pair); consecutive blocks in the order of the
+  // work items go to one XCD (block b runs on XCD b % 8), as in
+  // va_partial_kernel
+  const int items = f.total_work;   // blocks of this launch: ns * ceil(G / 2)
+  const int per_xcd = (items + 7) >> 3;
+  const int it = (block & 7) * per_xcd + (block >> 3);
+  if (it >= items) return;
+  const int r = 0;
+  const int G = f.g0;               // 64-row groups of the request
+  const int GW = (G + 1) >> 1;      // row pairs
+  const int s = it / GW;
+  const int gw = it - s * GW;
+  const int ns = f.ns0;
+  const int T = f.t0;
+  const int H = f.num_heads;
+  const int tb = 0;
+  const int rows_r = T * H;
+
+  if (tid == 0) sm.status_sh = 0u;
+  uint32_t st = 0u;
+  const int maxp = f.max_prefix0;
+  int L = f.prefix_len[r];
+  if (L < 0 || L > maxp) {
+    st |= VA_STATUS_BAD_PREFIX;
+    L = L < 0 ? 0 : maxp;
+  }
+  const int n = L + T;
+  const int tab0 = f.slot_indptr[r];
+  const int tab1 = f.slot_indptr[r + 1];
+  int n_valid = n;
+  if (tab0 < 0 || tab1 < tab0 || tab1 > f.slot_table_len || tab1 - tab0 < n) {
+    st |= VA_STATUS_SHORT_TABLE;
+    n_valid = (tab0 < 0 || tab1 < tab0 || tab0 >= f.slot_table_len)
+                  ? 0 : min(min(tab1, f.slot_table_len) - tab0, n);
+  }
+  // FUSED: the L prefix keys in ns slices of whole SPLIT_ALIGN blocks; the T
+  // draft keys go with the last slice
+  const int chunk = ((L + ns - 1) / ns + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
+  const int k0 = min(s * chunk, L);
+  const int k1 = min(n_valid, s == ns - 1 ? n : min(k0 + chunk, L));
+  const int ntiles = k1 > k0 ? (k1 - k0 + WTILE - 1) / WTILE : 0;
+  const int32_t* table = f.slot_table + (n_valid > 0 ? tab0 : 0);
+
+  auto issue_slots = [&](int u) {
+    if (wave == 0 && lane < WTILE) {
+      const int k = min(k0 + u * WTILE + lane, k1 - 1);
+      dma4_v(lds_addr(&sm.sring[u & (WSLOT_RING - 1)][0]), table + k);
+    }
+  };
+  if (ntiles > 0) {
+    issue_slots(0);
+    issue_slots(1);
+    issue_slots(2);
+  }
+  if (wave == 0) dma4_v(lds_addr(&sm.parents[0]), a.parent + tb + min(lane, T - 1));
+
+  // ---- Q: this wave's 32 rows, all 576 score columns, straight into VGPRs
+  // (B operand of S^T = K . Q^T: lane l holds row l % 32, columns
+  // 16 k + 8 (l / 32) .. +7 of k-step k).  Rows past the request's end read
+  // row 0: they repeat its scores and are never merged.
+  const int rho = gw * WROWS + wave * 32 + lrow;   // row of the request
+  const bool row_ok = rho < rows_r;
+  bf16x8 qf[QV];
+  {
+    const uint16_t* qrow = f.q + ((int64_t)tb * H + (row_ok ? rho : 0)) * DQK + 8 * lh;
+    // the tail k-steps into this wave's LDS area, lane l at 16 l (one copy each)
+#pragma unroll
+    for (int k = QV; k < QK_STEPS; ++k) dma16v(lds_addr(&sm.qt[wave][k - QV][0]), qrow + 16 * k);
+#pragma unroll
+    for (int k = 0; k < QV; ++k) qf[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k);
+  }
+
+  // ---- tile loader: wave w copies the 9 lines of tile keys 8 w .. 8 w + 7;
+  // lane l takes key 8 w + l / 8 and its piece (l % 8) ^ swz(key)
+  uint32_t bad = 0u;
+  struct WIssue {
+    const uint16_t* src;
+    uint32_t lds_w;
+  };
+  const int wkey = 8 * wave + (lane >> 3);
+  auto prepare = [&](int u, int slot, int buf) -> WIssue {
+    WIssue wi;
+    wi.src = copy_source(a.kv, a.num_slots, a.stride, slot, k0 + u * WTILE + wkey < k1, wkey,
+                         lane, bad);
+    wi.lds_w = lds_addr(tiles + buf * WBUF_ELEMS) + wave * CHUNK;
+    return wi;
+  };
+  auto issue_copy = [&](const WIssue& wi, int c) {
+    wdma_copy(c, wi.lds_w, wi.src, std::make_integer_sequence<int, WCOPIES>{});
+  };
+
+  f32x16 o[O_BLK];
+  float m_ref = -INFINITY;
+  float m_seen = -INFINITY;
+  float l_run = 0.f;
+  float lb_run = 0.f;
+  bf16x8 pown[2];
+
+  uint32_t kb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kb[i] = wpiece_off(lrow, 2 * i + lh);
+  uint32_t vb[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn)
+      vb[c][nn] = wpiece_off(8 * nn + 4 * lh + ((lane & 15) >> 2),
+                             4 * c + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + (lane & 1) * 8;
+  }
+  const int qkey = 4 * lh;   // tile key of register 4 qd + i is qkey + 8 qd + i
+
+  auto compute = [&](int t, int buf, uint64_t anc_row, bool first, const WIssue& nxt, bool sweep) {
+    const uint8_t* const bp = reinterpret_cast<const uint8_t*>(tiles + buf * WBUF_ELEMS);
+    const int kt = k0 + t * WTILE;
+    f32x16 sacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+    constexpr int QG = 4;
+    // per-tile LDS addresses of this lane's K pieces, opaque to the compiler so
+    // that each read is base + an instruction offset (no hoisted address per read)
+    uint32_t kbase[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kbase[i] = lds_addr(bp) + kb[i];
+      asm volatile("" : "+v"(kbase[i]));
+    }
+    auto load_k = [&](bf16x8* kf, bf16x8* qx, int k0s) {
+#pragma unroll
+      for (int kk = 0; kk < QG; ++kk) {
+        const int k = k0s + kk;
+        kf[kk] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            (uintptr_t)(kbase[k & 3] + WLINE * (k >> 2)));
+        if (k >= QV) qx[kk] = sm.qt[wave][k - QV][lane];
+      }
+    };
+    bf16x8 kfa[QG], kfb[QG], qxa[QG], qxb[QG];
+    load_k(kfa, qxa, 0);
+#pragma unroll
+    for (int g = 0; g < QK_STEPS / QG; ++g) {
+      bf16x8* cur = (g & 1) ? kfb : kfa;
+      bf16x8* ahead = (g & 1) ? kfa : kfb;
+      bf16x8* qcur = (g & 1) ? qxb : qxa;
+      bf16x8* qahead = (g & 1) ? qxa : qxb;
+      if (g + 1 < QK_STEPS / QG) load_k(ahead, qahead, (g + 1) * QG);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < QG; ++kk) {
+        const int k = g * QG + kk;
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[kk], k < QV ? qf[k < QV ? k : 0] : qcur[kk],
+                                                       sacc, 0, 0, 0);
+      }
+      issue_copy(nxt, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kt + WTILE > L || kt + WTILE > k1) {   // uniform
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kp = kt + qkey + 8 * (e >> 2) + (e & 3);
+        const int d = kp - L;
+        const bool in_tree = d < 0 || ((anc_row >> (d & 63)) & 1ull);
+        sacc[e] = (kp < k1 && in_tree) ? sacc[e] : -INFINITY;
+      }
+    }
+    float mx = sacc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                       __builtin_bit_cast(uint32_t, mx), false, false);
+      mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+    }
+    mx *= a.scale_log2;
+    m_seen = fmaxf(m_seen, mx);
+    if (sweep) return;
+    if (first) {
+      if (m_ref == -INFINITY) m_ref = mx;
+    } else if (mx > m_ref + REF_SLACK) {
+      sm.restart_sh[t & 1] = 1u;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ks + i], a.scale_log2, -m_use));
+      l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      bf16x2 pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = bf16x2{(__bf16)p[2 * i], (__bf16)p[2 * i + 1]};
+        lb_run = __builtin_amdgcn_fdot2_f32_bf16(pb[i], ones, lb_run, false);
+      }
+      pown[ks] = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, pb[0]),
+                                                   __builtin_bit_cast(uint32_t, pb[1]),
+                                                   __builtin_bit_cast(uint32_t, pb[2]),
+                                                   __builtin_bit_cast(uint32_t, pb[3])});
+    }
+  };
+
+  // O^T += V^T . P^T over the tile's 32 keys: 16 column blocks x 2 k-steps,
+  // V^T fragments by transpose reads one block ahead
+  auto value = [&](int buf) {
+    uint32_t vbase[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        vbase[c][nn] = lds_addr(tiles + buf * WBUF_ELEMS) + vb[c][nn];
+        asm volatile("" : "+v"(vbase[c][nn]));
+      }
+    }
+    auto load_v2 = [&](bf16x8* vf, int cb) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t off = (cb >> 1) * WLINE + j * (2 * CHUNK);
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vbase[cb & 1][0] + off));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vbase[cb & 1][1] + off));
+        const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        vf[j] = __builtin_bit_cast(bf16x8, v8);
+      }
+    };
+    bf16x8 vfa[2], vfb[2];
+    load_v2(vfa, 0);
+    // the probabilities were just written by vector ALU instructions
+    asm volatile("s_nop 4" : "+v"(pown[0]), "+v"(pown[1]));
+#pragma unroll
+    for (int cb = 0; cb < O_BLK; cb += 2) {
+      load_v2(vfb, cb + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mfma_acc(o[cb], vfa[j], pown[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cb + 2 < O_BLK) load_v2(vfa, cb + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mfma_acc(o[cb + 1], vfb[j], pown[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  uint64_t anc_row = 0ull;
+  for (int pass = 0;; ++pass) {
+    const bool sweep = pass == 1;
+    // accumulator writes after the last pass's accumulating MFMAs, and the
+    // first accumulating MFMA after the writes
+    if (pass > 0) acc_settle(o);
+#pragma unroll
+    for (int c = 0; c < O_BLK; ++c) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[c][e] = 0.f;
+    }
+    acc_settle(o);
+    l_run = 0.f;
+    lb_run = 0.f;
+    if (tid == 0) {
+      sm.restart_sh[0] = 0u;
+      sm.restart_sh[1] = 0u;
+    }
+    if (pass > 0) {
+      if (ntiles > 0) {
+        issue_slots(0);
+        issue_slots(1);
+        issue_slots(2);
+      }
+      vm_wait<0>();
+    } else {
+      // wave 0: slots 0, 1, 2 and the parents went out before its 36 Q copies and loads
+      vm_wait<QK_STEPS>();
+    }
+    __syncthreads();   // slots 0..2 (and parents) in LDS; status_sh, restart_sh set
+    if (ntiles > 0) {
+      const WIssue t0i = prepare(0, sm.sring[0][wkey], 0);
+#pragma unroll
+      for (int c = 0; c < WCOPIES; ++c) issue_copy(t0i, c);
+      const WIssue t1i = prepare(1, sm.sring[1][wkey], 1);
+#pragma unroll
+      for (int c = 0; c < WCOPIES; ++c) issue_copy(t1i, c);
+    }
+    if (pass == 0 && wave == 0) {
+      int p = lane < T ? sm.parents[lane] : -1;
+      if (p < -1 || p >= lane) {   // parents precede their children
+        st |= VA_STATUS_BAD_PARENT;
+        p = -1;
+      }
+      uint64_t m = lane < T ? 1ull << lane : 0ull;
+      int x = p;
+      while (__any(x >= 0)) {
+        const int nx = __shfl(p, x >= 0 ? x : 0);
+        if (x >= 0) {
+          m |= 1ull << x;
+          x = nx;
+        }
+      }
+      sm.anc[lane] = m;
+    }
+
+    bool restart = false;
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t landed (the copies of tile t + 1 may still be in flight)
+      vm_wait<WCOPIES>();
+      lds_barrier();   // tile t and slots t + 2 in LDS; every wave is done with tile t - 1
+      if (t == 0 && pass == 0) anc_row = row_ok ? sm.anc[rho / H] : 0ull;
+      // tile t - 1's restart requests: all written before the barrier above,
+      // and entry (t - 1) % 2 is not written again before the next barrier
+      if (pass == 0 && t > 0 &&
+          __builtin_amdgcn_readfirstlane(sm.restart_sh[(t - 1) & 1]) != 0u) {   // uniform
+        restart = true;
+        break;
+      }
+      const WIssue nxt = prepare(t + 2, sm.sring[(t + 2) & (WSLOT_RING - 1)][wkey], (t + 2) % WNBUF);
+      issue_slots(t + 3);
+      compute(t, t % WNBUF, anc_row, t == 0, nxt, sweep);
+      if (!sweep) value(t % WNBUF);
+    }
+    vm_wait<0>();
+    __syncthreads();
+    if (!restart) restart = sweep || (pass == 0 && (sm.restart_sh[0] | sm.restart_sh[1]) != 0u);
+    if (!restart) break;
+    m_ref = m_seen;
+    __syncthreads();
+  }
+  acc_settle(o);
+
+  // ---- store o / lb in fp16 as two virtual 64-row work items
+  {
+    const float l = l_run + __shfl_xor(l_run, 32);
+    const float lb = lb_run + __shfl_xor(lb_run, 32);
+    float amax = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < O_BLK; ++cb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[cb][e]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    int ex = 0;
+    float scale = 0.f;
+    if (lb > 0.f && amax > 0.f) {
+      ex = ilogbf(amax / lb) - 14;
+      scale = ldexpf(1.f / lb, -ex);
+    }
+    const int vg = 2 * gw + (wave >> 1);        // virtual row group
+    const int rh = wave & 1;
+    if (vg < G) {
+      const int w = s * G + vg;   // the 64-row work item
+      u32x2* po = reinterpret_cast<u32x2*>(a.part_o) + (int64_t)w * PART_VEC + rh * O_BLK * 4 * 64 + lane;
+#pragma unroll
+      for (int cb = 0; cb < O_BLK; ++cb) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f16x4 h = {(_Float16)(o[cb][4 * qd] * scale), (_Float16)(o[cb][4 * qd + 1] * scale),
+                           (_Float16)(o[cb][4 * qd + 2] * scale), (_Float16)(o[cb][4 * qd + 3] * scale)};
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h), &po[(cb * 4 + qd) * 64]);
+        }
+      }
+      if (lh == 0) {
+        const float lse2 = l > 0.f ? m_ref + log2f(l) : -INFINITY;
+        *reinterpret_cast<float2*>(a.part_lse + ((int64_t)w * ROWS + rh * 32 + lrow) * 2) =
+            make_float2(lse2, (float)ex);
+      }
+    }
+  }
+  st |= bad;
+  if (st) atomicOr(&sm.status_sh, st);
+  __syncthreads();
+  if (tid < 2) {
+    const int vg = 2 * gw + tid;
+    if (vg < G) a.status[s * G + vg] = sm.status_sh;
+  }
+}
+
+__global__ __launch_bounds__(THREADS, 1) void va_wide_kernel(
+    const int32_t* prefix_len, const int32_t* slot_indptr, const int32_t* slot_table,
+    const uint16_t* q, int32_t items, int32_t num_heads, int32_t slot_table_len, int32_t ns0,
+    int32_t g0, int32_t t0, int32_t max_prefix0, PartialArgs a) {
+  __shared__ WideSmem sm;
+  const Lead f{prefix_len, slot_indptr, slot_table, q, items, num_heads, slot_table_len,
+               ns0, g0, t0, max_prefix0};
+  wide_body(a, f, blockIdx.x, sm);
+}
+
 // Log-sum-exp merge of the splits.  One block per (request, row group, row
 // half, 32-column block, 4-column quad): 32 rows x 8 columns, read as one
 // contiguous 512-byte piece per split; with QPB = 4, all four quads of the
@@ -1206,6 +1676,10 @@ bool plan_ok(const va_plan* p) {
       p->rows_per_group != ROWS || p->tile_keys != TILE ||
       (p->mode != VA_MODE_FUSED && p->mode != VA_MODE_SPLIT_TREE))
     return false;
+  // 128-row blocks: one request, fused mode only
+  if (p->groups_per_block != 1 &&
+      (p->groups_per_block != 2 || p->num_requests != 1 || p->mode != VA_MODE_FUSED))
+    return false;
   // the derived tables must be the ones the planner writes: the kernels
   // index through them without further checks
   if (p->num_heads < 1 || p->work_begin[0] != 0 || p->tree_begin[0] != 0) return false;
@@ -1293,6 +1767,12 @@ int launch_partial(const va_plan* plan, const uint16_t* q, const uint16_t* kv_po
       hipLaunchKernelGGL(va_split_kernel<false>, dim3(grid + (unsigned)tree_blocks), dim3(THREADS),
                          0, st, prefix_len, slot_indptr, slot_table, q, tree_blocks, a.total_work,
                          a.num_heads, slot_table_len, ns0, g0, t0, mp0, a);
+  } else if (plan->groups_per_block == 2) {
+    // one block per (split, row pair), in the XCD order of the work items
+    const int blocks = ns0 * ((g0 + 1) / 2);
+    const unsigned wgrid = 8u * (unsigned)((blocks + 7) / 8);
+    hipLaunchKernelGGL(va_wide_kernel, dim3(wgrid), dim3(THREADS), 0, st, prefix_len, slot_indptr,
+                       slot_table, q, blocks, a.num_heads, slot_table_len, ns0, g0, t0, mp0, a);
   } else {
     if (plan->num_requests == 1)
       hipLaunchKernelGGL(va_partial_kernel<true>, dim3(grid), dim3(THREADS), 0, st, prefix_len,
@@ -1401,8 +1881,12 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
                         const int32_t* h_num_tree, int32_t num_cus, uint32_t flags,
                         va_plan* plan, size_t* workspace_bytes) {
   if (h_prefix_len == nullptr || h_num_tree == nullptr || plan == nullptr) return VA_ERR_NULL;
-  if ((flags & ~VA_PLAN_SPLIT_TREE) != 0u) return VA_ERR_SHAPE;
+  if ((flags & ~(VA_PLAN_SPLIT_TREE | VA_PLAN_ROWS64 | VA_PLAN_ROWS128)) != 0u) return VA_ERR_SHAPE;
   const bool split_tree = (flags & VA_PLAN_SPLIT_TREE) != 0u;
+  const bool rows64 = (flags & VA_PLAN_ROWS64) != 0u;
+  const bool rows128 = (flags & VA_PLAN_ROWS128) != 0u;
+  if (rows64 && rows128) return VA_ERR_SHAPE;
+  if (rows128 && (split_tree || num_requests != 1)) return VA_ERR_SHAPE;
   if (num_requests < 1 || num_requests > VA_MAX_REQUESTS) return VA_ERR_SHAPE;
   if (num_heads < 1 || num_heads > VA_MAX_HEADS) return VA_ERR_SHAPE;
   if (num_cus < 0) return VA_ERR_SHAPE;
@@ -1424,8 +1908,14 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   p.tile_keys = TILE;
   p.num_cus = num_cus;
   p.mode = split_tree ? VA_MODE_SPLIT_TREE : VA_MODE_FUSED;
+  // 128-row blocks (va_wide_kernel) for one request with many rows
+  const bool wide = rows128 || (!rows64 && !split_tree && num_requests == 1 &&
+                                (int64_t)h_num_tree[0] * num_heads >= WIDE_MIN_ROWS);
+  const int gpb = wide ? 2 : 1;
+  p.groups_per_block = gpb;
 
-  // Split count: balance prefix keys x row groups over the compute units.
+  // Split count: balance prefix keys x blocks per split (row groups, or row
+  // pairs with 128-row blocks) over the compute units.
   // The draft keys (at most one tile) go with each request's last split in
   // the fused mode, and to the tree block, one more split per request run by
   // its own small kernel, in the split-tree mode.
@@ -1433,7 +1923,7 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   int64_t cus = num_cus;
   for (int r = 0; r < num_requests; ++r) {
     const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
-    units += groups * (int64_t)h_prefix_len[r];
+    units += (groups + gpb - 1) / gpb * (int64_t)h_prefix_len[r];
     if (split_tree) cus -= groups;   // compute units the tree-block work items occupy
   }
   if (cus < 1) cus = 1;
@@ -1469,7 +1959,7 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
       for (int r = 0; r < num_requests; ++r) {
         const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
         const int64_t ns = nsplit_of(r, keys_per_item);
-        items += groups * ns;
+        items += (groups + gpb - 1) / gpb * ns;   // blocks
         more |= ns > 1;
       }
       if (items <= cus || !more) break;

@@ -65,7 +65,14 @@ def test_plan_long_prefix_h8_t16():
 
 
 def test_plan_full_heads_and_ragged_batch():
+    # 16 x 64 = 1024 rows: 128-row blocks, 8 row pairs; 8 * 200000 / 256 =
+    # 6250 keys per block, rounded up to 6272 (whole tiles) -> 32 splits of
+    # 8 blocks = 256 blocks, 512 work items of 64 rows
     p = _plan(64, [200000], [16])
+    assert p.groups_per_block == 2
+    assert p.num_groups[0] == 16 and p.nsplit[0] == 32 and p.total_work == 512
+    p = va.verify_attn_plan(64, [200000], [16], num_cus=256, rows=64)
+    assert p.groups_per_block == 1
     assert p.num_groups[0] == 16 and p.nsplit[0] == 16 and p.total_work == 256
     p = _plan(16, [1024, 16384, 65536, 131072], [32] * 4)
     assert [p.num_groups[r] for r in range(4)] == [8] * 4
@@ -253,6 +260,44 @@ def test_plan_ex_rejects_unknown_flags_and_bad_modes():
     assert _run(lib, bad) == -5
 
 
+def test_plan_block_size_rule_and_flags():
+    """128-row blocks for one request in the fused mode with T * H >= 1024
+    rows; the flags force either size where it applies and are refused where
+    it does not."""
+    assert _plan(8, [65536], [16]).groups_per_block == 1          # 128 rows
+    assert _plan(32, [65536], [31]).groups_per_block == 1         # 992 rows
+    assert _plan(32, [65536], [32]).groups_per_block == 2         # 1024 rows
+    assert _plan(64, [100, 100], [16, 16]).groups_per_block == 1  # two requests
+    assert va.verify_attn_plan(64, [65536], [16], num_cus=256,
+                               split_tree=True).groups_per_block == 1
+    p = va.verify_attn_plan(8, [65536], [16], num_cus=256, rows=128)
+    # one row pair: 65536 / 256 = 256 keys per block -> 256 splits
+    assert p.groups_per_block == 2 and p.nsplit[0] == 256 and p.total_work == 512
+    assert va.verify_attn_plan(32, [65536], [32], num_cus=256, rows=64).groups_per_block == 1
+    lib = va.load_library()
+    b = binding.VaPlan()
+    for B, flags in ((1, binding.VA_PLAN_ROWS64 | binding.VA_PLAN_ROWS128),
+                     (1, binding.VA_PLAN_ROWS128 | binding.VA_PLAN_SPLIT_TREE),
+                     (2, binding.VA_PLAN_ROWS128), (1, 8)):
+        pl = np.array([100] * B, np.int32)
+        nt = np.array([4] * B, np.int32)
+        assert lib.verify_attn_plan_ex(B, 8, pl.ctypes.data_as(ctypes.c_void_p),
+                                       nt.ctypes.data_as(ctypes.c_void_p), 256, flags,
+                                       ctypes.byref(b), None) == -2, (B, flags)
+
+
+@pytest.mark.parametrize("gpb,B", [(0, 1), (3, 1), (2, 2)])
+def test_run_refuses_a_tampered_block_size(gpb, B):
+    """groups_per_block is 1, or 2 for a single request in the fused mode;
+    any other value is refused before a launch (no GPU)."""
+    lib = va.load_library()
+    plan = _plan(8, [100] * B, [4] * B)
+    bad = binding.VaPlan()
+    ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
+    bad.groups_per_block = gpb
+    assert _run(lib, bad) == -5
+
+
 @pytest.mark.parametrize("split_tree", [False, True])
 def test_plans_fit_the_compute_units(split_tree):
     """Rounded-up split counts must not add up to more work items than CUs
@@ -268,10 +313,12 @@ def test_plans_fit_the_compute_units(split_tree):
     for H, L, T, cus in cases:
         p = va.verify_attn_plan(H, L, T, num_cus=cus, split_tree=split_tree)
         groups = [(t * H + 63) // 64 for t in T]
+        gpb = p.groups_per_block                       # blocks hold 1 or 2 row groups
+        blocks = [-(-g // gpb) for g in groups]
         ns = list(p.nsplit[:len(L)])
         prefix_splits = [n - 1 for n in ns] if split_tree else ns
         budget = cus - (sum(groups) if split_tree else 0)
-        prefix_items = sum(g * n for g, n in zip(groups, prefix_splits))
+        prefix_items = sum(b * n for b, n in zip(blocks, prefix_splits))
         assert prefix_items <= max(budget, 1) or all(n == 1 for n in prefix_splits), (H, L, T, cus, ns)
         assert p.total_work == sum(g * n for g, n in zip(groups, ns))
 

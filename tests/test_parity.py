@@ -50,10 +50,13 @@ class Dev:
         self.parent = _t(wl.parent)
 
 
-def run_gpu(wl, d=None, plan=None, prefix_host=None):
+def run_gpu(wl, d=None, plan=None, prefix_host=None, rows=None):
+    """rows: None (the planner's block size), 64 or 128 (forced)."""
     d = d or Dev(wl)
     plan = plan or va.verify_attn_plan(wl.num_heads, wl.prefix_len if prefix_host is None
-                                       else prefix_host, wl.num_tree)
+                                       else prefix_host, wl.num_tree, rows=rows)
+    if rows is not None:
+        assert plan.groups_per_block == rows // 64
     ws = va.workspace_for(plan, DEV)
     out, lse = va.verify_attn(d.q, d.kv, d.table, d.indptr, d.prefix, d.parent, wl.sm_scale,
                               num_tree=wl.num_tree, prefix_len_host=wl.prefix_len, plan=plan,
@@ -79,12 +82,13 @@ def bf16_representation_error(ref):
 REPR_FROM = 2.0
 
 
-def check(wl, out, lse, rows=None, what=""):
+def check(wl, out, lse, rows=None, what="", ref=None):
     """Compare with the oracle, element by element.
     Output: |out - oracle| <= 1e-2 wherever |oracle| < 2; where |oracle| >= 2,
     |out - oracle| - (bf16 representation error of the oracle value) <= 1e-2.
-    LSE: |lse - oracle| <= 1e-3 on every row."""
-    ref, ref_lse = oracle.verify_attn_workload(wl, rows=rows)
+    LSE: |lse - oracle| <= 1e-3 on every row.  ref: the oracle's (out, lse)
+    for this workload, if already computed."""
+    ref, ref_lse = ref if ref is not None else oracle.verify_attn_workload(wl, rows=rows)
     got = out.float().cpu().numpy().reshape(-1, 512).astype(np.float64)
     gl = lse.cpu().numpy().reshape(-1)
     ref = ref.reshape(-1, 512)
@@ -111,14 +115,18 @@ def check(wl, out, lse, rows=None, what=""):
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_config_parity_all_rows(idx):
     """The five workloads, every output row against the oracle (the full-head
-    and ragged ones take the oracle about 12 s and 6 s on 16 host cores)."""
+    and ragged ones take the oracle about 12 s and 6 s on 16 host cores).
+    The full-head workload gets 128-row blocks from the planner; it is also
+    run with 64-row blocks against the same oracle result."""
     wl = inputs.make_config(idx)
     say(f"config {idx} {wl.name}: H={wl.num_heads} T={wl.num_tree.tolist()} "
         f"L={wl.prefix_len.tolist()}")
-    out, lse, status, plan = run_gpu(wl)
-    assert status == 0
-    say(f"  nsplit={plan.splits()} work={plan.total_work}")
-    check(wl, out, lse, what=f"config {idx}")
+    ref = oracle.verify_attn_workload(wl)
+    for rows in ((None, 64) if idx == 4 else (None,)):
+        out, lse, status, plan = run_gpu(wl, rows=rows)
+        assert status == 0
+        say(f"  rows={64 * plan.groups_per_block} nsplit={plan.splits()} work={plan.total_work}")
+        check(wl, out, lse, what=f"config {idx}", ref=ref)
 
 
 # --------------------------------------------------------------------------- shapes and edges
@@ -139,57 +147,67 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"H{c[0]}_T{c[1]}_L{c[2]}_{c[3]}")
-def test_edge_shapes(case):
+# 128-row blocks take one request only
+EDGE_ROWS = [(c, None) for c in EDGE] + [(c, 128) for c in EDGE if len(c[1]) == 1]
+
+
+@pytest.mark.parametrize("case,rows", EDGE_ROWS,
+                         ids=lambda c: f"H{c[0]}_T{c[1]}_L{c[2]}_{c[3]}" if isinstance(c, tuple)
+                         else f"rows{c}")
+def test_edge_shapes(case, rows):
     H, T, L, tree = case
     wl = inputs.make_workload("edge", H, T, L, 4096, seed=sum(L) + H, tree=tree,
                               table="interleaved" if len(T) > 1 else "scattered")
-    say(f"edge H={H} T={T} L={L} {tree}")
-    out, lse, status, _ = run_gpu(wl)
+    say(f"edge H={H} T={T} L={L} {tree} rows={rows}")
+    out, lse, status, _ = run_gpu(wl, rows=rows)
     assert status == 0
     check(wl, out, lse, what="edge")
 
 
+@pytest.mark.parametrize("rows", [None, 128])
 @pytest.mark.parametrize("nsplit", [1, 2, 3, 7, 64, 128])
-def test_split_count_does_not_change_the_result(nsplit, monkeypatch):
+def test_split_count_does_not_change_the_result(nsplit, rows, monkeypatch):
     wl = inputs.make_workload("ns", 8, [16], [4096], 16384, seed=3)
     monkeypatch.setenv("VA_NSPLIT", str(nsplit))
-    say(f"VA_NSPLIT={nsplit}")
-    out, lse, status, plan = run_gpu(wl)
+    say(f"VA_NSPLIT={nsplit} rows={rows}")
+    out, lse, status, plan = run_gpu(wl, rows=rows)
     assert status == 0 and plan.nsplit[0] == nsplit
     check(wl, out, lse, what=f"nsplit {nsplit}")
 
 
-def test_split_of_draft_keys_only(monkeypatch):
+@pytest.mark.parametrize("rows", [None, 128])
+def test_split_of_draft_keys_only(rows, monkeypatch):
     """L = 1024, T = 64, 9 splits: the last split holds the 64 draft keys
     alone, and with a star tree node j sees only key L + j there (and all of
     the prefix elsewhere).  Every row still counts its own key."""
     monkeypatch.setenv("VA_NSPLIT", "9")
     wl = inputs.make_workload("draft_split", 4, [64], [1024], 4096, seed=71, tree="star")
-    out, lse, status, plan = run_gpu(wl)
+    out, lse, status, plan = run_gpu(wl, rows=rows)
     assert status == 0 and plan.splits() == [9]
     check(wl, out, lse, what="draft-only split, star tree")
 
 
-def test_graph_bound_above_actual_prefix():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_graph_bound_above_actual_prefix(rows):
     """Plan with an upper bound, run with a shorter device prefix length."""
     wl = inputs.make_workload("bound", 8, [16], [3000], 8192, seed=5)
     say("plan for L<=5000, run L=3000")
-    out, lse, status, plan = run_gpu(wl, prefix_host=[5000])
+    out, lse, status, plan = run_gpu(wl, prefix_host=[5000], rows=rows)
     assert status == 0
     check(wl, out, lse, what="bound")
 
 
 # --------------------------------------------------------------------------- coverage closed forms
+@pytest.mark.parametrize("rows", [None, 128])
 @pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000])
-def test_zero_query_counts_every_visible_key(L):
+def test_zero_query_counts_every_visible_key(L, rows):
     """q = 0: lse = ln(number of visible keys) exactly; one key more or less
     moves it by >= 1e-3 at these lengths."""
     H, T = 4, 16
     wl = inputs.make_workload("q0", H, [T], [L], 4096, seed=100 + L,
                               q_override=np.zeros((T, H, 576), dtype=np.uint16))
-    say(f"q=0 L={L}")
-    out, lse, status, _ = run_gpu(wl)
+    say(f"q=0 L={L} rows={rows}")
+    out, lse, status, _ = run_gpu(wl, rows=rows)
     assert status == 0
     vis = oracle.tree_visibility(wl.parent)
     expect = np.log(L + vis.sum(1))
@@ -208,8 +226,9 @@ def _needle(L, T, key, seed):
     return wl
 
 
+@pytest.mark.parametrize("rows", [None, 128])
 @pytest.mark.parametrize("nsplit", [1, 5])
-def test_needle_at_tile_and_split_edges(nsplit, monkeypatch):
+def test_needle_at_tile_and_split_edges(nsplit, rows, monkeypatch):
     """A dominant key at every tile/split edge must reach every node's output."""
     L, T = 2000, 16
     monkeypatch.setenv("VA_NSPLIT", str(nsplit))
@@ -219,7 +238,7 @@ def test_needle_at_tile_and_split_edges(nsplit, monkeypatch):
                       [c + d for c in range(0, L, chunk) for d in (-1, 0) if 0 <= c + d < L]))
     for key in keys:
         wl = _needle(L, T, key, seed=7)
-        out, lse, status, _ = run_gpu(wl)
+        out, lse, status, _ = run_gpu(wl, rows=rows)
         assert status == 0
         v = inputs.bf16_to_f32(wl.kv_pool[wl.slot_table[key]])[:512]
         err = np.abs(out.float().cpu().numpy() - v).max()
@@ -227,13 +246,14 @@ def test_needle_at_tile_and_split_edges(nsplit, monkeypatch):
         assert err <= OUT_TOL
 
 
-def test_needle_on_draft_nodes_respects_the_tree():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_needle_on_draft_nodes_respects_the_tree(rows):
     L, T = 700, 32
     base = inputs.make_workload("nd", 2, [T], [L], 4 * (L + T) + 64, seed=9)
     vis = oracle.tree_visibility(base.parent)
     for j in range(T):
         wl = _needle(L, T, L + j, seed=9)
-        out, lse, status, _ = run_gpu(wl)
+        out, lse, status, _ = run_gpu(wl, rows=rows)
         assert status == 0
         v = inputs.bf16_to_f32(wl.kv_pool[wl.slot_table[L + j]])[:512]
         got = out.float().cpu().numpy()
@@ -262,15 +282,18 @@ def _rising(L, T, step, seed):
     return wl
 
 
+@pytest.mark.parametrize("rows", [None, 128])
 @pytest.mark.parametrize("nsplit", [1, 3])
-def test_scores_rising_past_the_reference_on_every_tile(nsplit, monkeypatch):
+def test_scores_rising_past_the_reference_on_every_tile(nsplit, rows, monkeypatch):
     """Tile maxima 100 log2 units apart over 12 tiles: each tile beats the
     previous one by more than the fixed-reference slack (64), so a split
     must find its exact max before its final pass.  The result is still the
-    plain softmax attention of the oracle, with finite values everywhere."""
+    plain softmax attention of the oracle, with finite values everywhere.
+    (128-row blocks step over 32-key tiles: every second one beats the
+    previous by that much.)"""
     monkeypatch.setenv("VA_NSPLIT", str(nsplit))
     wl = _rising(L=64 * 12, T=4, step=100.0, seed=11)
-    out, lse, status, plan = run_gpu(wl)
+    out, lse, status, plan = run_gpu(wl, rows=rows)
     assert status == 0
     check(wl, out, lse, what=f"rising scores nsplit={plan.splits()}")
 
@@ -299,64 +322,69 @@ def test_maximum_head_count_and_tree():
     check(wl, out, lse, what=f"H=1024 T=64 work={plan.total_work}")
 
 
-def test_maximum_split_count(monkeypatch):
+@pytest.mark.parametrize("rows", [None, 128])
+def test_maximum_split_count(rows, monkeypatch):
     """VA_MAX_SPLITS (256) splits of one request: the reduce's largest
     instantiation merges them."""
     monkeypatch.setenv("VA_NSPLIT", str(binding.VA_MAX_SPLITS))
     wl = inputs.make_workload("max_s", 8, [16], [12000], 32768, seed=66)
-    out, lse, status, plan = run_gpu(wl)
+    out, lse, status, plan = run_gpu(wl, rows=rows)
     assert status == 0
     assert plan.splits() == [binding.VA_MAX_SPLITS]
     check(wl, out, lse, what=f"nsplit={plan.splits()}")
 
 
 # --------------------------------------------------------------------------- bit-exactness
-def test_permuted_pool_gives_identical_bits():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_permuted_pool_gives_identical_bits(rows):
     wl = inputs.make_workload("perm", 8, [16], [5000], 16384, seed=13)
-    out, lse, _, _ = run_gpu(wl)
+    out, lse, _, _ = run_gpu(wl, rows=rows)
     pi = np.random.default_rng(1).permutation(wl.num_slots)
     pool2 = np.empty_like(wl.kv_pool)
     pool2[pi] = wl.kv_pool
     wl2 = inputs.Workload(**{**wl.__dict__, "kv_pool": pool2,
                              "slot_table": pi[wl.slot_table].astype(np.int32)})
-    out2, lse2, _, _ = run_gpu(wl2)
+    out2, lse2, _, _ = run_gpu(wl2, rows=rows)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
-def test_unused_slots_poisoned_with_nan_are_never_read():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_unused_slots_poisoned_with_nan_are_never_read(rows):
     wl = inputs.make_workload("poison", 8, [16], [3000], 8192, seed=17)
-    out, lse, _, _ = run_gpu(wl)
+    out, lse, _, _ = run_gpu(wl, rows=rows)
     pool = wl.kv_pool.copy()
     unused = np.setdiff1d(np.arange(wl.num_slots), wl.slot_table)
     pool[unused] = 0x7FC0
     d = Dev(wl, kv_pool=_bf16(pool))
-    out2, lse2, status, _ = run_gpu(wl, d=d)
+    out2, lse2, status, _ = run_gpu(wl, d=d, rows=rows)
     assert status == 0
     assert torch.isfinite(out2.float()).all()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
-def test_repeated_calls_are_bitwise_identical():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_repeated_calls_are_bitwise_identical(rows):
     wl = inputs.make_workload("rep", 8, [16], [10000], 16384, seed=19)
     d = Dev(wl)
-    a, la, _, plan = run_gpu(wl, d=d)
+    a, la, _, plan = run_gpu(wl, d=d, rows=rows)
     for _ in range(3):
         b, lb, _, _ = run_gpu(wl, d=d, plan=plan)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
         assert torch.equal(la.view(torch.int32), lb.view(torch.int32))
 
 
-def test_padded_row_stride_matches_dense_pool():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_padded_row_stride_matches_dense_pool(rows):
     wl = inputs.make_workload("stride", 4, [8], [900], 2048, seed=23)
-    out, lse, _, _ = run_gpu(wl)
+    out, lse, _, _ = run_gpu(wl, rows=rows)
     wide = np.full((wl.num_slots, 640), 0x7FC0, dtype=np.uint16)
     wide[:, :576] = wl.kv_pool
     kv_wide = _bf16(wide)
     d = Dev(wl, kv_pool=kv_wide)
     assert kv_wide.stride(0) == 640
-    out2, lse2, status, _ = run_gpu(wl, d=d)
+    out2, lse2, status, _ = run_gpu(wl, d=d, rows=rows)
     assert status == 0
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
@@ -376,10 +404,11 @@ def test_gather_rows_is_bit_exact():
     assert (got[~ok] == 0x7FC0).all()
 
 
-def test_graph_capture_replays_bit_exact_and_follows_device_lengths():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_graph_capture_replays_bit_exact_and_follows_device_lengths(rows):
     wl = inputs.make_workload("graph", 8, [16], [6000], 16384, seed=31)
     d = Dev(wl)
-    plan = va.verify_attn_plan(8, [6000], [16])
+    plan = va.verify_attn_plan(8, [6000], [16], rows=rows)
     ws = va.workspace_for(plan, DEV)
     out = torch.empty((16, 8, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((16, 8), dtype=torch.float32, device=DEV)
@@ -451,13 +480,14 @@ def test_device_data_errors_poison_only_their_request():
     assert torch.equal(o[:8].view(torch.int16), good_o[:8].view(torch.int16))
 
 
-def test_single_request_table_offset_and_device_errors():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_single_request_table_offset_and_device_errors(rows):
     """A single request (the launches that take its values as preloaded
     kernel arguments): its table slice may start anywhere in the slot table,
     and a device prefix above the planned bound or a short slice still poison
     the rows and set the status bits."""
     wl = inputs.make_workload("one", 8, [16], [700], 4096, seed=41, table="interleaved")
-    good_o, good_l, status, plan = run_gpu(wl)
+    good_o, good_l, status, plan = run_gpu(wl, rows=rows)
     assert status == 0
     check(wl, good_o, good_l, what="offset 0")
     # the same slots behind 37 unrelated entries

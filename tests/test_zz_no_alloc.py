@@ -15,7 +15,7 @@ import torch
 import speculative_tree_verify_mla_amd as va
 from speculative_tree_verify_mla_amd import binding, inputs
 
-VA_STATIC_SCRATCH_BYTES = 16909312
+VA_STATIC_SCRATCH_BYTES = 33818624
 
 
 def _fake(addr):
@@ -41,16 +41,17 @@ def test_static_entry_refusals_before_any_launch(monkeypatch):
     ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
     bad.magic = 0
     assert _static(lib, bad) == -5
-    # 64 rows x 64 heads = 64 row groups; 5 splits each = 320 work items,
-    # more than the scratch holds
-    monkeypatch.setenv("VA_NSPLIT", "5")
-    big = va.verify_attn_plan(64, [4096], [64], num_cus=256)
-    assert big.total_work == 320 and big.workspace_bytes > VA_STATIC_SCRATCH_BYTES
-    assert _static(lib, big) == -4
-    # the largest plan the scratch holds: 256 work items
-    monkeypatch.setenv("VA_NSPLIT", "4")
+    # 64 rows x 64 heads = 64 row groups; 9 splits each = 576 work items,
+    # more than the scratch holds (with either block size)
+    monkeypatch.setenv("VA_NSPLIT", "9")
+    for rows in (64, 128):
+        big = va.verify_attn_plan(64, [4096], [64], num_cus=256, rows=rows)
+        assert big.total_work == 576 and big.workspace_bytes > VA_STATIC_SCRATCH_BYTES
+        assert _static(lib, big) == -4
+    # the largest plan the scratch holds: 512 work items
+    monkeypatch.setenv("VA_NSPLIT", "8")
     edge = va.verify_attn_plan(64, [4096], [64], num_cus=256)
-    assert edge.total_work == 256 and edge.workspace_bytes == VA_STATIC_SCRATCH_BYTES
+    assert edge.total_work == 512 and edge.workspace_bytes == VA_STATIC_SCRATCH_BYTES
 
 
 def _t(a):
@@ -63,7 +64,8 @@ def _bf16(a):
 
 @pytest.mark.gpu
 def test_static_scratch_matches_run_and_reduce_on_calls_in_a_row():
-    # 256 work items (the scratch's maximum), then 228, then 32: each call
+    # the 64-head workload (128-row blocks, 512 work items: the scratch's
+    # maximum), the 65k workload (256) and the 4k workload (64): each call
     # leaves the scratch holding its own partials for the next one
     for idx in (4, 3, 2):
         wl = inputs.make_config(idx)
