@@ -1030,8 +1030,8 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
     n_valid = (tab0 < 0 || tab1 < tab0 || tab0 >= f.slot_table_len)
                   ? 0 : min(min(tab1, f.slot_table_len) - tab0, n);
   }
-  // FUSED: the L prefix keys in ns slices of whole SPLIT_ALIGN blocks; the T
-  // draft keys go with the last slice
+  // the split ranges of the fused mode: the L prefix keys in ns slices of
+  // whole SPLIT_ALIGN blocks; the T draft keys go with the last slice
   const int chunk = ((L + ns - 1) / ns + SPLIT_ALIGN - 1) / SPLIT_ALIGN * SPLIT_ALIGN;
   const int k0 = min(s * chunk, L);
   const int k1 = min(n_valid, s == ns - 1 ? n : min(k0 + chunk, L));
@@ -1321,7 +1321,7 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
   }
   acc_settle(o);
 
-  // ---- store o / lb in fp16 as two virtual 64-row work items
+  // ---- store o / lb in fp16 as the block's two 64-row work items
   {
     const float l = l_run + __shfl_xor(l_run, 32);
     const float lb = lb_run + __shfl_xor(lb_run, 32);
@@ -1338,7 +1338,7 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
       ex = ilogbf(amax / lb) - 14;
       scale = ldexpf(1.f / lb, -ex);
     }
-    const int vg = 2 * gw + (wave >> 1);        // virtual row group
+    const int vg = 2 * gw + (wave >> 1);        // this wave's row group
     const int rh = wave & 1;
     if (vg < G) {
       const int w = s * G + vg;   // the 64-row work item
