@@ -156,12 +156,14 @@ typedef struct va_plan {
  * the compute units.  The environment variable VA_NSPLIT, read here
  * only, forces one split count for every request (for tuning sweeps; with
  * VA_PLAN_SPLIT_TREE it is the count of prefix splits).
- * A single request in the fused mode with T*H >= 1024 rows gets 128-row
- * blocks (groups_per_block = 2): one block runs the two row groups 2j and
- * 2j+1 of a split, so each KV row enters a compute unit once per 128 rows,
- * and the splits are balanced over ceil(groups / 2) blocks per split (about
- * twice the splits of 64-row blocks).  The work items, the workspace and the
- * merge stay those of 64-row groups.
+ * A single request in the fused mode with at least two row groups gets
+ * 128-row blocks (groups_per_block = 2) when ceil(groups / 2) * L_r >=
+ * 2048 * num_cus, i.e. when each block's share of the prefix is at least
+ * 2048 keys: one block runs the two row groups 2j and 2j+1 of a split, so
+ * each KV row enters a compute unit once per 128 rows, and the splits are
+ * balanced over ceil(groups / 2) blocks per split (about twice the splits of
+ * 64-row blocks).  The work items, the workspace and the merge stay those of
+ * 64-row groups.  VA_NSPLIT does not enter this choice.
  * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_HIP (device query failed).
  */
 int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,

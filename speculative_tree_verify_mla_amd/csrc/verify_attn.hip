@@ -911,8 +911,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
 // ---- 128-row blocks over 32-key tiles (one request, fused mode) -----------
 // The streaming design loads each KV tile once and computes every head on it
 // ("The Execution Phase", section "The Core Design: A Streaming Flash
-// Attention Kernel").  With many rows per request (T * H >= WIDE_MIN_ROWS) a
-// block here takes the two 64-row work items of a split that share a row
+// Attention Kernel").  With many rows and long splits (a block's share of
+// the prefix at least WIDE_MIN_KEYS keys, see verify_attn_plan_ex) a block
+// here takes the two 64-row work items of a split that share a row
 // pair (groups 2 gw and 2 gw + 1), so every KV row of the split enters the
 // CU once for 128 rows instead of once per 64.  Wave w owns rows
 // 32 w .. 32 w + 31 of the block entirely: the score of every key of a tile
@@ -930,7 +931,10 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
 // probabilities (written by VALU instructions) get their wait states before
 // the first value MFMA reads them.
 constexpr int WROWS = 128;
-constexpr int WIDE_MIN_ROWS = 1024;   // rows per request from which the planner picks these blocks
+// Prefix keys per block from which the planner picks these blocks.  Below,
+// the doubled split count (partials to write and merge) and the larger Q
+// prologue per block cost more than the halved KV ingest saves.
+constexpr int WIDE_MIN_KEYS = 2048;
 constexpr int WTILE = 32;
 constexpr int WLINE = (WTILE / 8) * CHUNK;      // one line of all keys of a tile: 4 KB
 constexpr int WBUF_BYTES = NLINE * WLINE;       // 36,864 B
@@ -1908,9 +1912,15 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   p.tile_keys = TILE;
   p.num_cus = num_cus;
   p.mode = split_tree ? VA_MODE_SPLIT_TREE : VA_MODE_FUSED;
-  // 128-row blocks (va_wide_kernel) for one request with many rows
-  const bool wide = rows128 || (!rows64 && !split_tree && num_requests == 1 &&
-                                (int64_t)h_num_tree[0] * num_heads >= WIDE_MIN_ROWS);
+  // 128-row blocks (va_wide_kernel) for one request with at least two row
+  // groups when a block would get at least WIDE_MIN_KEYS prefix keys: the
+  // row pairs' share of the CUs, before any split-count override
+  bool wide = rows128;
+  if (!rows64 && !rows128 && !split_tree && num_requests == 1) {
+    const int64_t groups = ((int64_t)h_num_tree[0] * num_heads + ROWS - 1) / ROWS;
+    const int64_t pairs = (groups + 1) / 2;
+    wide = groups >= 2 && pairs * (int64_t)h_prefix_len[0] >= (int64_t)WIDE_MIN_KEYS * num_cus;
+  }
   const int gpb = wide ? 2 : 1;
   p.groups_per_block = gpb;
 

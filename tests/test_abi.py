@@ -260,20 +260,30 @@ def test_plan_ex_rejects_unknown_flags_and_bad_modes():
     assert _run(lib, bad) == -5
 
 
-def test_plan_block_size_rule_and_flags():
-    """128-row blocks for one request in the fused mode with T * H >= 1024
-    rows; the flags force either size where it applies and are refused where
-    it does not."""
-    assert _plan(8, [65536], [16]).groups_per_block == 1          # 128 rows
-    assert _plan(32, [65536], [31]).groups_per_block == 1         # 992 rows
-    assert _plan(32, [65536], [32]).groups_per_block == 2         # 1024 rows
-    assert _plan(64, [100, 100], [16, 16]).groups_per_block == 1  # two requests
-    assert va.verify_attn_plan(64, [65536], [16], num_cus=256,
+def test_plan_block_size_rule_and_flags(monkeypatch):
+    """128-row blocks for one request in the fused mode with at least two row
+    groups when a block's share of the prefix, ceil(groups / 2) * L / CUs,
+    is at least 2048 keys; the flags force either size where it applies and
+    are refused where it does not."""
+    gpb = lambda H, L, T, cus=256: _plan(H, L, T, cus).groups_per_block
+    assert gpb(8, [65536], [16]) == 1             # 1 row pair: 256 keys per block
+    assert gpb(32, [65536], [16]) == 1            # 4 pairs: 1024
+    assert gpb(64, [16384], [16]) == 1            # 8 pairs: 512
+    assert gpb(64, [65536], [16]) == 2            # 8 pairs: 2048
+    assert gpb(32, [200000], [16]) == 2           # 4 pairs: 3125
+    assert gpb(64, [200000], [16]) == 2
+    assert gpb(32, [65536], [16], cus=128) == 2   # the same rows on fewer CUs: 2048
+    assert gpb(1, [200000], [64]) == 1            # one row group
+    assert gpb(64, [200000, 200000], [16, 16]) == 1    # two requests
+    assert va.verify_attn_plan(64, [200000], [16], num_cus=256,
                                split_tree=True).groups_per_block == 1
+    monkeypatch.setenv("VA_NSPLIT", "200")        # a forced split count does not decide it
+    assert gpb(64, [200000], [16]) == 2 and gpb(64, [16384], [16]) == 1
+    monkeypatch.delenv("VA_NSPLIT")
     p = va.verify_attn_plan(8, [65536], [16], num_cus=256, rows=128)
     # one row pair: 65536 / 256 = 256 keys per block -> 256 splits
     assert p.groups_per_block == 2 and p.nsplit[0] == 256 and p.total_work == 512
-    assert va.verify_attn_plan(32, [65536], [32], num_cus=256, rows=64).groups_per_block == 1
+    assert va.verify_attn_plan(64, [200000], [16], num_cus=256, rows=64).groups_per_block == 1
     lib = va.load_library()
     b = binding.VaPlan()
     for B, flags in ((1, binding.VA_PLAN_ROWS64 | binding.VA_PLAN_ROWS128),
