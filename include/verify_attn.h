@@ -130,7 +130,7 @@ typedef struct va_plan {
 /* verify_attn_plan_ex flags */
 #define VA_PLAN_SPLIT_TREE 1u   /* plan VA_MODE_SPLIT_TREE instead of VA_MODE_FUSED */
 #define VA_PLAN_ROWS64 2u       /* 64-row blocks (groups_per_block = 1) whatever the row count */
-#define VA_PLAN_ROWS128 4u      /* 128-row blocks (groups_per_block = 2); one request, fused mode only */
+#define VA_PLAN_ROWS128 4u      /* 128-row blocks (groups_per_block = 2); fused mode only */
 
 /*
  * verify_attn_plan - size the split-KV schedule and the workspace (host only).
@@ -156,14 +156,14 @@ typedef struct va_plan {
  * the compute units.  The environment variable VA_NSPLIT, read here
  * only, forces one split count for every request (for tuning sweeps; with
  * VA_PLAN_SPLIT_TREE it is the count of prefix splits).
- * A single request in the fused mode with at least two row groups gets
- * 128-row blocks (groups_per_block = 2) when ceil(groups / 2) * L_r >=
- * 2048 * num_cus, i.e. when each block's share of the prefix is at least
- * 2048 keys: one block runs the two row groups 2j and 2j+1 of a split, so
- * each KV row enters a compute unit once per 128 rows, and the splits are
- * balanced over ceil(groups / 2) blocks per split (about twice the splits of
- * 64-row blocks).  The work items, the workspace and the merge stay those of
- * 64-row groups.  VA_NSPLIT does not enter this choice.
+ * In the fused mode, when every request has at least two row groups and
+ * sum_r ceil(groups_r / 2) * L_r >= 2048 * num_cus (each block's share of
+ * the prefix is at least 2048 keys), the plan uses 128-row blocks
+ * (groups_per_block = 2): one block runs the two row groups 2j and 2j+1 of
+ * a split, so each KV row enters a compute unit once per 128 rows, and the
+ * splits are balanced over ceil(groups / 2) blocks per split (about twice
+ * the splits of 64-row blocks).  The work items, the workspace and the
+ * merge stay those of 64-row groups.  VA_NSPLIT does not enter this choice.
  * Errors: VA_ERR_NULL, VA_ERR_SHAPE, VA_ERR_HIP (device query failed).
  */
 int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
@@ -175,9 +175,9 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
  * verify_attn_plan (VA_MODE_FUSED); VA_PLAN_SPLIT_TREE plans the
  * split-verify decomposition (VA_MODE_SPLIT_TREE): nsplit[r] counts the
  * prefix splits plus the one tree-block split.  VA_PLAN_ROWS64 and
- * VA_PLAN_ROWS128 override the row-count rule for the block size; both
- * together, or VA_PLAN_ROWS128 with more than one request or with
- * VA_PLAN_SPLIT_TREE, are VA_ERR_SHAPE, as are unknown flag bits.  Other
+ * VA_PLAN_ROWS128 override that rule for the block size; both together, or
+ * VA_PLAN_ROWS128 with VA_PLAN_SPLIT_TREE, are VA_ERR_SHAPE, as are unknown
+ * flag bits.  Other
  * arguments and errors as verify_attn_plan.
  */
 int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,

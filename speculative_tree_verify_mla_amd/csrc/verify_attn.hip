@@ -908,7 +908,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
   if (tid == 0) a.status[w] = status_sh;
 }
 
-// ---- 128-row blocks over 32-key tiles (one request, fused mode) -----------
+// ---- 128-row blocks over 32-key tiles (fused mode) ---------------------------
 // The streaming design loads each KV tile once and computes every head on it
 // ("The Execution Phase", section "The Core Design: A Streaming Flash
 // Attention Kernel").  With many rows and long splits (a block's share of
@@ -990,6 +990,7 @@ __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf1
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+template <bool ONE>
 __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, int block,
                                           WideSmem& sm) {
   uint16_t* const tiles = sm.tiles;
@@ -999,27 +1000,35 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
   const int lrow = lane & 31;
   const int lh = lane >> 5;
 
-  // blocks ordered (split, row pair); consecutive blocks in the order of the
-  // work items go to one XCD (block b runs on XCD b % 8), as in
-  // va_partial_kernel
-  const int items = f.total_work;   // blocks of this launch: ns * ceil(G / 2)
+  // blocks ordered (request, split, row pair); consecutive blocks in that
+  // order go to one XCD (block b runs on XCD b % 8), as in va_partial_kernel
+  const int items = f.total_work;   // blocks of this launch: sum of ns * ceil(G / 2)
   const int per_xcd = (items + 7) >> 3;
-  const int it = (block & 7) * per_xcd + (block >> 3);
+  int it = (block & 7) * per_xcd + (block >> 3);
   if (it >= items) return;
-  const int r = 0;
-  const int G = f.g0;               // 64-row groups of the request
-  const int GW = (G + 1) >> 1;      // row pairs
+  int r = 0;
+  if (!ONE) {
+    for (;;) {   // uniform
+      const int nb = a.nsplit[r] * ((a.num_groups[r] + 1) >> 1);
+      if (r + 1 >= a.num_requests || it < nb) break;
+      it -= nb;
+      ++r;
+    }
+  }
+  const int G = ONE ? f.g0 : a.num_groups[r];   // 64-row groups of the request
+  const int GW = (G + 1) >> 1;                    // row pairs
   const int s = it / GW;
   const int gw = it - s * GW;
-  const int ns = f.ns0;
-  const int T = f.t0;
+  const int ns = ONE ? f.ns0 : a.nsplit[r];
+  const int T = ONE ? f.t0 : a.num_tree[r];
   const int H = f.num_heads;
-  const int tb = 0;
+  const int tb = ONE ? 0 : a.tree_begin[r];
+  const int wb = ONE ? 0 : a.work_begin[r];       // the request's first work item
   const int rows_r = T * H;
 
   if (tid == 0) sm.status_sh = 0u;
   uint32_t st = 0u;
-  const int maxp = f.max_prefix0;
+  const int maxp = ONE ? f.max_prefix0 : a.max_prefix[r];
   int L = f.prefix_len[r];
   if (L < 0 || L > maxp) {
     st |= VA_STATUS_BAD_PREFIX;
@@ -1345,7 +1354,7 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
     const int vg = 2 * gw + (wave >> 1);        // this wave's row group
     const int rh = wave & 1;
     if (vg < G) {
-      const int w = s * G + vg;   // the 64-row work item
+      const int w = wb + s * G + vg;   // the 64-row work item
       u32x2* po = reinterpret_cast<u32x2*>(a.part_o) + (int64_t)w * PART_VEC + rh * O_BLK * 4 * 64 + lane;
 #pragma unroll
       for (int cb = 0; cb < O_BLK; ++cb) {
@@ -1368,10 +1377,11 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
   __syncthreads();
   if (tid < 2) {
     const int vg = 2 * gw + tid;
-    if (vg < G) a.status[s * G + vg] = sm.status_sh;
+    if (vg < G) a.status[wb + s * G + vg] = sm.status_sh;
   }
 }
 
+template <bool ONE>
 __global__ __launch_bounds__(THREADS, 1) void va_wide_kernel(
     const int32_t* prefix_len, const int32_t* slot_indptr, const int32_t* slot_table,
     const uint16_t* q, int32_t items, int32_t num_heads, int32_t slot_table_len, int32_t ns0,
@@ -1379,7 +1389,7 @@ __global__ __launch_bounds__(THREADS, 1) void va_wide_kernel(
   __shared__ WideSmem sm;
   const Lead f{prefix_len, slot_indptr, slot_table, q, items, num_heads, slot_table_len,
                ns0, g0, t0, max_prefix0};
-  wide_body(a, f, blockIdx.x, sm);
+  wide_body<ONE>(a, f, blockIdx.x, sm);
 }
 
 // Log-sum-exp merge of the splits.  One block per (request, row group, row
@@ -1680,9 +1690,8 @@ bool plan_ok(const va_plan* p) {
       p->rows_per_group != ROWS || p->tile_keys != TILE ||
       (p->mode != VA_MODE_FUSED && p->mode != VA_MODE_SPLIT_TREE))
     return false;
-  // 128-row blocks: one request, fused mode only
-  if (p->groups_per_block != 1 &&
-      (p->groups_per_block != 2 || p->num_requests != 1 || p->mode != VA_MODE_FUSED))
+  // 128-row blocks: fused mode only
+  if (p->groups_per_block != 1 && (p->groups_per_block != 2 || p->mode != VA_MODE_FUSED))
     return false;
   // the derived tables must be the ones the planner writes: the kernels
   // index through them without further checks
@@ -1772,11 +1781,19 @@ int launch_partial(const va_plan* plan, const uint16_t* q, const uint16_t* kv_po
                          0, st, prefix_len, slot_indptr, slot_table, q, tree_blocks, a.total_work,
                          a.num_heads, slot_table_len, ns0, g0, t0, mp0, a);
   } else if (plan->groups_per_block == 2) {
-    // one block per (split, row pair), in the XCD order of the work items
-    const int blocks = ns0 * ((g0 + 1) / 2);
+    // one block per (request, split, row pair), in XCD order (see wide_body)
+    int blocks = 0;
+    for (int r = 0; r < plan->num_requests; ++r)
+      blocks += plan->nsplit[r] * ((plan->num_groups[r] + 1) / 2);
     const unsigned wgrid = 8u * (unsigned)((blocks + 7) / 8);
-    hipLaunchKernelGGL(va_wide_kernel, dim3(wgrid), dim3(THREADS), 0, st, prefix_len, slot_indptr,
-                       slot_table, q, blocks, a.num_heads, slot_table_len, ns0, g0, t0, mp0, a);
+    if (plan->num_requests == 1)
+      hipLaunchKernelGGL(va_wide_kernel<true>, dim3(wgrid), dim3(THREADS), 0, st, prefix_len,
+                         slot_indptr, slot_table, q, blocks, a.num_heads, slot_table_len, ns0, g0,
+                         t0, mp0, a);
+    else
+      hipLaunchKernelGGL(va_wide_kernel<false>, dim3(wgrid), dim3(THREADS), 0, st, prefix_len,
+                         slot_indptr, slot_table, q, blocks, a.num_heads, slot_table_len, ns0, g0,
+                         t0, mp0, a);
   } else {
     if (plan->num_requests == 1)
       hipLaunchKernelGGL(va_partial_kernel<true>, dim3(grid), dim3(THREADS), 0, st, prefix_len,
@@ -1890,7 +1907,7 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   const bool rows64 = (flags & VA_PLAN_ROWS64) != 0u;
   const bool rows128 = (flags & VA_PLAN_ROWS128) != 0u;
   if (rows64 && rows128) return VA_ERR_SHAPE;
-  if (rows128 && (split_tree || num_requests != 1)) return VA_ERR_SHAPE;
+  if (rows128 && split_tree) return VA_ERR_SHAPE;
   if (num_requests < 1 || num_requests > VA_MAX_REQUESTS) return VA_ERR_SHAPE;
   if (num_heads < 1 || num_heads > VA_MAX_HEADS) return VA_ERR_SHAPE;
   if (num_cus < 0) return VA_ERR_SHAPE;
@@ -1912,14 +1929,19 @@ int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* 
   p.tile_keys = TILE;
   p.num_cus = num_cus;
   p.mode = split_tree ? VA_MODE_SPLIT_TREE : VA_MODE_FUSED;
-  // 128-row blocks (va_wide_kernel) for one request with at least two row
-  // groups when a block would get at least WIDE_MIN_KEYS prefix keys: the
-  // row pairs' share of the CUs, before any split-count override
+  // 128-row blocks (va_wide_kernel) when every request has at least two row
+  // groups and a block would get at least WIDE_MIN_KEYS prefix keys: the
+  // row pairs' prefix keys over the CUs, before any split-count override
   bool wide = rows128;
-  if (!rows64 && !rows128 && !split_tree && num_requests == 1) {
-    const int64_t groups = ((int64_t)h_num_tree[0] * num_heads + ROWS - 1) / ROWS;
-    const int64_t pairs = (groups + 1) / 2;
-    wide = groups >= 2 && pairs * (int64_t)h_prefix_len[0] >= (int64_t)WIDE_MIN_KEYS * num_cus;
+  if (!rows64 && !rows128 && !split_tree) {
+    bool pairs_only = true;
+    int64_t pair_keys = 0;
+    for (int r = 0; r < num_requests; ++r) {
+      const int64_t groups = ((int64_t)h_num_tree[r] * num_heads + ROWS - 1) / ROWS;
+      pairs_only &= groups >= 2;
+      pair_keys += (groups + 1) / 2 * (int64_t)h_prefix_len[r];
+    }
+    wide = pairs_only && pair_keys >= (int64_t)WIDE_MIN_KEYS * num_cus;
   }
   const int gpb = wide ? 2 : 1;
   p.groups_per_block = gpb;

@@ -74,7 +74,7 @@ def test_plan_full_heads_and_ragged_batch():
     p = va.verify_attn_plan(64, [200000], [16], num_cus=256, rows=64)
     assert p.groups_per_block == 1
     assert p.num_groups[0] == 16 and p.nsplit[0] == 16 and p.total_work == 256
-    p = _plan(16, [1024, 16384, 65536, 131072], [32] * 4)
+    p = va.verify_attn_plan(16, [1024, 16384, 65536, 131072], [32] * 4, num_cus=256, rows=64)
     assert [p.num_groups[r] for r in range(4)] == [8] * 4
     keys = [1024 + 32, 16384 + 32, 65536 + 32, 131072 + 32]
     per = -(-8 * sum(keys) // 256)
@@ -86,6 +86,13 @@ def test_plan_full_heads_and_ragged_batch():
     assert p.splits() == [-(-k // per) for k in keys] == [1, 3, 9, 18]
     assert p.work_begin[4] == p.total_work == 8 * sum(p.splits()) == 248
     assert [p.tree_begin[r] for r in range(5)] == [0, 32, 64, 96, 128]
+    # by default 128-row blocks: 4 row pairs per request, prefix keys x pairs
+    # over 256 CUs = 3344 keys per block, whole tiles 3392 -> [1, 5, 20, 39]
+    # = 260 blocks; lengthened to 3456 -> [1, 5, 19, 38] = 252 blocks
+    p = _plan(16, [1024, 16384, 65536, 131072], [32] * 4)
+    assert p.groups_per_block == 2
+    assert p.splits() == [1, 5, 19, 38]
+    assert p.work_begin[4] == p.total_work == 8 * sum(p.splits()) == 504
 
 
 def test_plan_small_inputs_keep_a_minimum_split_length():
@@ -274,7 +281,9 @@ def test_plan_block_size_rule_and_flags(monkeypatch):
     assert gpb(64, [200000], [16]) == 2
     assert gpb(32, [65536], [16], cus=128) == 2   # the same rows on fewer CUs: 2048
     assert gpb(1, [200000], [64]) == 1            # one row group
-    assert gpb(64, [200000, 200000], [16, 16]) == 1    # two requests
+    assert gpb(64, [200000, 200000], [16, 16]) == 2    # two requests: 2 x 8 pairs x 200000
+    assert gpb(64, [200000, 200000], [16, 1]) == 1     # a request with one row group
+    assert gpb(16, [1024, 16384, 65536, 131072], [32] * 4) == 2   # 4 x 4 pairs x 214016 keys
     assert va.verify_attn_plan(64, [200000], [16], num_cus=256,
                                split_tree=True).groups_per_block == 1
     monkeypatch.setenv("VA_NSPLIT", "200")        # a forced split count does not decide it
@@ -286,9 +295,11 @@ def test_plan_block_size_rule_and_flags(monkeypatch):
     assert va.verify_attn_plan(64, [200000], [16], num_cus=256, rows=64).groups_per_block == 1
     lib = va.load_library()
     b = binding.VaPlan()
+    p = va.verify_attn_plan(8, [100, 2000], [4, 16], num_cus=256, rows=128)
+    assert p.groups_per_block == 2 and p.num_requests == 2
     for B, flags in ((1, binding.VA_PLAN_ROWS64 | binding.VA_PLAN_ROWS128),
                      (1, binding.VA_PLAN_ROWS128 | binding.VA_PLAN_SPLIT_TREE),
-                     (2, binding.VA_PLAN_ROWS128), (1, 8)):
+                     (2, binding.VA_PLAN_ROWS128 | binding.VA_PLAN_SPLIT_TREE), (1, 8)):
         pl = np.array([100] * B, np.int32)
         nt = np.array([4] * B, np.int32)
         assert lib.verify_attn_plan_ex(B, 8, pl.ctypes.data_as(ctypes.c_void_p),
@@ -296,12 +307,12 @@ def test_plan_block_size_rule_and_flags(monkeypatch):
                                        ctypes.byref(b), None) == -2, (B, flags)
 
 
-@pytest.mark.parametrize("gpb,B", [(0, 1), (3, 1), (2, 2)])
+@pytest.mark.parametrize("gpb,B", [(0, 1), (3, 2), (2, 1), (2, 2)])
 def test_run_refuses_a_tampered_block_size(gpb, B):
-    """groups_per_block is 1, or 2 for a single request in the fused mode;
-    any other value is refused before a launch (no GPU)."""
+    """groups_per_block is 1, or 2 in the fused mode; any other value, or 2
+    in a split-tree plan, is refused before a launch (no GPU)."""
     lib = va.load_library()
-    plan = _plan(8, [100] * B, [4] * B)
+    plan = va.verify_attn_plan(8, [100] * B, [4] * B, num_cus=256, split_tree=gpb == 2)
     bad = binding.VaPlan()
     ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
     bad.groups_per_block = gpb

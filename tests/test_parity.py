@@ -116,13 +116,14 @@ def check(wl, out, lse, rows=None, what="", ref=None):
 def test_config_parity_all_rows(idx):
     """The five workloads, every output row against the oracle (the full-head
     and ragged ones take the oracle about 12 s and 6 s on 16 host cores).
-    The full-head workload gets 128-row blocks from the planner; it is also
-    run with 64-row blocks against the same oracle result."""
+    The full-head workload and the ragged batch get 128-row blocks from the
+    planner; they are also run with 64-row blocks against the same oracle
+    result."""
     wl = inputs.make_config(idx)
     say(f"config {idx} {wl.name}: H={wl.num_heads} T={wl.num_tree.tolist()} "
         f"L={wl.prefix_len.tolist()}")
     ref = oracle.verify_attn_workload(wl)
-    for rows in ((None, 64) if idx == 4 else (None,)):
+    for rows in ((None, 64) if idx in (4, 5) else (None,)):
         out, lse, status, plan = run_gpu(wl, rows=rows)
         assert status == 0
         say(f"  rows={64 * plan.groups_per_block} nsplit={plan.splits()} work={plan.total_work}")
@@ -147,8 +148,7 @@ EDGE = [
 ]
 
 
-# 128-row blocks take one request only
-EDGE_ROWS = [(c, None) for c in EDGE] + [(c, 128) for c in EDGE if len(c[1]) == 1]
+EDGE_ROWS = [(c, None) for c in EDGE] + [(c, 128) for c in EDGE]
 
 
 @pytest.mark.parametrize("case,rows", EDGE_ROWS,
@@ -299,7 +299,8 @@ def test_scores_rising_past_the_reference_on_every_tile(nsplit, rows, monkeypatc
 
 
 # --------------------------------------------------------------------------- maximum sizes
-def test_maximum_request_count():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_maximum_request_count(rows):
     """VA_MAX_REQUESTS (64) requests of mixed tree sizes and prefixes in one
     call: every request's rows against the oracle."""
     rng = np.random.default_rng(64)
@@ -308,7 +309,7 @@ def test_maximum_request_count():
     L = rng.integers(0, 1500, size=B).tolist()
     wl = inputs.make_workload("max_b", 2, T, L, 2 * (sum(T) + sum(L)) + 64, seed=64,
                               table="interleaved")
-    out, lse, status, plan = run_gpu(wl)
+    out, lse, status, plan = run_gpu(wl, rows=rows)
     assert status == 0
     check(wl, out, lse, what=f"B={B} work={plan.total_work}")
 
@@ -447,9 +448,10 @@ def test_graph_capture_replays_bit_exact_and_follows_device_lengths(rows):
 
 
 # --------------------------------------------------------------------------- device-data errors
-def test_device_data_errors_poison_only_their_request():
+@pytest.mark.parametrize("rows", [None, 128])
+def test_device_data_errors_poison_only_their_request(rows):
     wl = inputs.make_workload("err", 4, [8, 8], [300, 200], 4096, seed=37, table="interleaved")
-    good_o, good_l, status, plan = run_gpu(wl)
+    good_o, good_l, status, plan = run_gpu(wl, rows=rows)
     assert status == 0
     cases = []
     t = wl.slot_table.copy()
