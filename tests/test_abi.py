@@ -411,3 +411,34 @@ def test_build_tree_rows_argument_errors_before_launch():
     assert call((13, 0)) == -2
     assert call((11, f(4104))) == -3            # src not 16-byte aligned
     assert call((12, f(8200))) == -3            # dst
+
+
+def test_128_row_block_map_covers_every_work_item_once():
+    """The 128-row kernel's block order (XCD-interleaved, then request, split,
+    row pair, as va_wide_kernel walks it) restated on the host over random
+    plans: every 64-row work item of the plan is written by exactly one
+    block, and no block addresses a split or row pair outside its request."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        B = int(rng.integers(1, 65))
+        H = int(rng.integers(1, 65))
+        T = [int(x) for x in rng.integers(1, 65, B)]
+        L = [int(x) for x in rng.integers(0, 300000, B)]
+        p = va.verify_attn_plan(H, L, T, num_cus=int(rng.choice([32, 100, 256, 304])), rows=128)
+        ns, G = list(p.nsplit[:B]), list(p.num_groups[:B])
+        blocks = sum(n * ((g + 1) // 2) for n, g in zip(ns, G))
+        per_xcd = (blocks + 7) >> 3
+        written = []
+        for blk in range(8 * per_xcd):
+            it = (blk & 7) * per_xcd + (blk >> 3)
+            if it >= blocks:
+                continue
+            r = 0
+            while r + 1 < B and it >= ns[r] * ((G[r] + 1) >> 1):
+                it -= ns[r] * ((G[r] + 1) >> 1)
+                r += 1
+            gw_count = (G[r] + 1) >> 1
+            s, gw = divmod(it, gw_count)
+            assert s < ns[r]
+            written += [p.work_begin[r] + s * G[r] + vg for vg in (2 * gw, 2 * gw + 1) if vg < G[r]]
+        assert sorted(written) == list(range(p.total_work))
