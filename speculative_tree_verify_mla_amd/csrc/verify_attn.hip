@@ -920,7 +920,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs& a, const Lead& f
 // over all 576 columns (Q k-steps 0 .. QV-1 in VGPRs, the rest from LDS),
 // its own softmax, and all 512 output columns (accumulators in the 256
 // AGPRs).  No probabilities change hands, so a tile needs one barrier.
-// Three 32-key tile buffers keep two tiles in flight.  The partials are
+// Two 32-key tile buffers: a tile's copies go out during the score phase of
+// the tile before (with three buffers and two tiles in flight, more of Q
+// had to stay in registers and the kernel spilled more).  The partials are
 // written as the two 64-row work items in the layout of va_partial_kernel,
 // so the merge is the same.
 //
@@ -939,10 +941,10 @@ constexpr int WTILE = 32;
 constexpr int WLINE = (WTILE / 8) * CHUNK;      // one line of all keys of a tile: 4 KB
 constexpr int WBUF_BYTES = NLINE * WLINE;       // 36,864 B
 constexpr int WBUF_ELEMS = WBUF_BYTES / 2;
-constexpr int WNBUF = 3;                        // two tiles in flight while one is consumed
+constexpr int WNBUF = 2;                        // the next tile in flight while one is consumed
 constexpr int WCOPIES = NLINE;                  // copies per wave per tile: 9 lines of its 8 keys
 constexpr int WSLOT_RING = 4;
-constexpr int QV = 24;   // score k-steps whose Q fragments stay in VGPRs; the rest are read from LDS
+constexpr int QV = 16;   // score k-steps whose Q fragments stay in VGPRs; the rest are read from LDS
 
 struct WideSmem {
   __attribute__((aligned(16))) uint16_t tiles[WNBUF * WBUF_ELEMS];
@@ -1060,7 +1062,6 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
   if (ntiles > 0) {
     issue_slots(0);
     issue_slots(1);
-    issue_slots(2);
   }
   if (wave == 0) dma4_v(lds_addr(&sm.parents[0]), a.parent + tb + min(lane, T - 1));
 
@@ -1273,21 +1274,17 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
       if (ntiles > 0) {
         issue_slots(0);
         issue_slots(1);
-        issue_slots(2);
       }
       vm_wait<0>();
     } else {
-      // wave 0: slots 0, 1, 2 and the parents went out before its 36 Q copies and loads
+      // wave 0: slots 0, 1 and the parents went out before its 36 Q copies and loads
       vm_wait<QK_STEPS>();
     }
-    __syncthreads();   // slots 0..2 (and parents) in LDS; status_sh, restart_sh set
+    __syncthreads();   // slots 0, 1 (and parents) in LDS; status_sh, restart_sh set
     if (ntiles > 0) {
       const WIssue t0i = prepare(0, sm.sring[0][wkey], 0);
 #pragma unroll
       for (int c = 0; c < WCOPIES; ++c) issue_copy(t0i, c);
-      const WIssue t1i = prepare(1, sm.sring[1][wkey], 1);
-#pragma unroll
-      for (int c = 0; c < WCOPIES; ++c) issue_copy(t1i, c);
     }
     if (pass == 0 && wave == 0) {
       int p = lane < T ? sm.parents[lane] : -1;
@@ -1309,9 +1306,9 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
 
     bool restart = false;
     for (int t = 0; t < ntiles; ++t) {
-      // tile t landed (the copies of tile t + 1 may still be in flight)
-      vm_wait<WCOPIES>();
-      lds_barrier();   // tile t and slots t + 2 in LDS; every wave is done with tile t - 1
+      // tile t (and the slots of tile t + 1) landed: nothing else is in flight
+      vm_wait<0>();
+      lds_barrier();   // tile t and slots t + 1 in LDS; every wave is done with tile t - 1
       if (t == 0 && pass == 0) anc_row = row_ok ? sm.anc[rho / H] : 0ull;
       // tile t - 1's restart requests: all written before the barrier above,
       // and entry (t - 1) % 2 is not written again before the next barrier
@@ -1320,8 +1317,9 @@ __device__ __forceinline__ void wide_body(const PartialArgs& a, const Lead& f, i
         restart = true;
         break;
       }
-      const WIssue nxt = prepare(t + 2, sm.sring[(t + 2) & (WSLOT_RING - 1)][wkey], (t + 2) % WNBUF);
-      issue_slots(t + 3);
+      // tile t + 1 goes into the buffer tile t - 1 left
+      const WIssue nxt = prepare(t + 1, sm.sring[(t + 1) & (WSLOT_RING - 1)][wkey], (t + 1) % WNBUF);
+      issue_slots(t + 2);
       compute(t, t % WNBUF, anc_row, t == 0, nxt, sweep);
       if (!sweep) value(t % WNBUF);
     }
