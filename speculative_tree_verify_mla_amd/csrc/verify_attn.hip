@@ -1830,11 +1830,12 @@ int launch_reduce(const va_plan* plan, const char* ws, uint16_t* out, float* lse
     groups += plan->num_groups[r];
     max_ns = max(max_ns, plan->nsplit[r]);
   }
-  // With few splits and more one-quad blocks than one round of the CUs
-  // holds (eight four-wave blocks each), a block takes all four quads of a
-  // 32-column block: one round of blocks instead of several.  The output is
-  // the same bit for bit (same splits per wave, same summation order).
-  const bool wide = max_ns <= 32 && groups * RED_PIECES > 8 * plan->num_cus;
+  // With up to 64 splits (four-wave blocks) and more one-quad blocks than
+  // one round of the CUs holds (eight four-wave blocks each), a block takes
+  // all four quads of a 32-column block: one round of blocks instead of
+  // several.  The output is the same bit for bit (same splits per wave, same
+  // summation order).
+  const bool quads = max_ns <= 64 && groups * RED_PIECES > 8 * plan->num_cus;
   const bool one = plan->num_requests == 1;
   const int ns0 = plan->nsplit[0], g0 = plan->num_groups[0];
   const int rows0 = plan->num_tree[0] * plan->num_heads;
@@ -1849,10 +1850,11 @@ int launch_reduce(const va_plan* plan, const char* ws, uint16_t* out, float* lse
   };
 #define VA_RED(M) launch(va_reduce_kernel<M, 1, true>, va_reduce_kernel<M, 1, false>, red_threads(M), 1)
 #define VA_RED4(M) launch(va_reduce_kernel<M, 4, true>, va_reduce_kernel<M, 4, false>, red_threads(M), 4)
-  if (max_ns <= 16 && wide) VA_RED4(16);
+  if (max_ns <= 16 && quads) VA_RED4(16);
   else if (max_ns <= 16) VA_RED(16);
-  else if (max_ns <= 32 && wide) VA_RED4(32);
+  else if (max_ns <= 32 && quads) VA_RED4(32);
   else if (max_ns <= 32) VA_RED(32);
+  else if (max_ns <= 64 && quads) VA_RED4(64);
   else if (max_ns <= 64) VA_RED(64);
   else if (max_ns <= 128) VA_RED(128);
   else VA_RED(VA_MAX_SPLITS);
