@@ -175,10 +175,9 @@ int verify_attn_plan(int32_t num_requests, int32_t num_heads, const int32_t* h_p
  * verify_attn_plan (VA_MODE_FUSED); VA_PLAN_SPLIT_TREE plans the
  * split-verify decomposition (VA_MODE_SPLIT_TREE): nsplit[r] counts the
  * prefix splits plus the one tree-block split.  VA_PLAN_ROWS64 and
- * VA_PLAN_ROWS128 override that rule for the block size; both together, or
- * VA_PLAN_ROWS128 with VA_PLAN_SPLIT_TREE, are VA_ERR_SHAPE, as are unknown
- * flag bits.  Other
- * arguments and errors as verify_attn_plan.
+ * VA_PLAN_ROWS128 override the block-size rule of verify_attn_plan; both
+ * together, or VA_PLAN_ROWS128 with VA_PLAN_SPLIT_TREE, are VA_ERR_SHAPE, as
+ * are unknown flag bits.  Other arguments and errors as verify_attn_plan.
  */
 int verify_attn_plan_ex(int32_t num_requests, int32_t num_heads, const int32_t* h_prefix_len,
                         const int32_t* h_num_tree, int32_t num_cus, uint32_t flags,
