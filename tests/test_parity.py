@@ -335,6 +335,19 @@ def test_maximum_split_count(rows, monkeypatch):
     check(wl, out, lse, what=f"nsplit={plan.splits()}")
 
 
+def test_merge_with_four_quad_blocks_up_to_64_splits(monkeypatch):
+    """One request with 32 row groups and 40 splits: the merge takes four
+    quads per block (more one-quad blocks than one round of the CUs, at most
+    64 splits).  Both block sizes against one oracle result."""
+    monkeypatch.setenv("VA_NSPLIT", "40")
+    wl = inputs.make_workload("quads", 64, [32], [10000], 16384, seed=67)
+    ref = oracle.verify_attn_workload(wl)
+    for rows in (64, 128):
+        out, lse, status, plan = run_gpu(wl, rows=rows)
+        assert status == 0 and plan.splits() == [40] and plan.num_groups[0] == 32
+        check(wl, out, lse, what=f"40 splits, 32 row groups, rows={rows}", ref=ref)
+
+
 # --------------------------------------------------------------------------- bit-exactness
 @pytest.mark.parametrize("rows", [None, 128])
 def test_permuted_pool_gives_identical_bits(rows):
